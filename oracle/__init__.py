@@ -1,0 +1,110 @@
+"""CPU oracle for the gated delta-rule recurrence -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The GPU library and its Python binding never
+import, load or call it, and it shares no code with them.
+
+``run`` wraps the double-precision token loop in ``gdn_oracle.c``:
+per head, the d_v x d_k state follows the gated delta rule of
+"Qwen3.8-27B 架构深读" (feifeigd.github.io, 2026-08-17), section 三
+(Gated DeltaNet): recall ``S k`` from the ungated previous state, gate the
+state by ``g``, add ``beta (v - recall) k^T``, and read out ``o = S q`` from
+the updated state.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn_oracle.so")
+
+_libs = {}
+
+
+def load(path=LIB_PATH):
+    """Load (once per path) an oracle shared library and declare its entry point."""
+    lib = _libs.get(path)
+    if lib is not None:
+        return lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"oracle library {path} is not built; run oracle/build.py")
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int64)
+    lib.gdn_oracle_run.restype = ctypes.c_int
+    lib.gdn_oracle_run.argtypes = [dp, dp, dp, dp, dp, ip, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   dp, dp, dp, ctypes.c_int]
+    _libs[path] = lib
+    return lib
+
+
+def default_threads():
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def run(q, k, v, g, beta, cu_seqlens=None, s_init=None, threads=None, lib_path=LIB_PATH):
+    """Run the recurrence over a packed batch.
+
+    q, k: [N, H, dk]; v: [N, H, dv]; g, beta: [N, H]; any real dtype (converted
+    exactly to float64).  cu_seqlens: [n_seq + 1] integer offsets, or None for a
+    single sequence.  s_init: [n_seq, H, dv, dk] or None (zeros).
+    Returns (o [N, H, dv], s_final [n_seq, H, dv, dk]) as float64.
+    """
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    N, H, dk = k.shape
+    dv = v.shape[2]
+    assert q.shape == (N, H, dk) and v.shape[:2] == (N, H), "q/k/v shapes disagree"
+    assert g.shape == (N, H) and beta.shape == (N, H), "g/beta must be [N, H]"
+    if cu_seqlens is None:
+        cu = None
+        n_seq = 1
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        n_seq = cu.shape[0] - 1
+    s0 = None if s_init is None else _f64(s_init)
+    if s0 is not None:
+        assert s0.shape == (n_seq, H, dv, dk), "s_init must be [n_seq, H, dv, dk]"
+    o = np.zeros((N, H, dv), dtype=np.float64)
+    s_final = np.zeros((n_seq, H, dv, dk), dtype=np.float64)
+    lib = load(lib_path)
+    cu_ptr = None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    rc = lib.gdn_oracle_run(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu_ptr,
+                            n_seq, N, H, dk, dv, _ptr(s0), _ptr(o), _ptr(s_final),
+                            int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"gdn_oracle_run rejected its arguments (code {rc})")
+    return o, s_final
+
+
+def run_decode(q, k, v, g, beta, s_init, threads=None, lib_path=LIB_PATH):
+    """Oracle for repeated single-token steps on a batch of states.
+
+    q, k: [steps, B, H, dk]; v: [steps, B, H, dv]; g, beta: [steps, B, H];
+    s_init: [B, H, dv, dk].  Step t of sequence b is token t of sequence b, so
+    this is the packed-batch recurrence with each sequence's tokens made
+    contiguous.  Returns (o [steps, B, H, dv], s_final [B, H, dv, dk]).
+    """
+    q, k, v = (np.asarray(x) for x in (q, k, v))
+    g, beta = np.asarray(g), np.asarray(beta)
+    steps, B, H, dk = k.shape
+    dv = v.shape[3]
+    pack = lambda x: np.ascontiguousarray(np.swapaxes(x, 0, 1)).reshape((B * steps,) + x.shape[2:])
+    cu = np.arange(B + 1, dtype=np.int64) * steps
+    o, s = run(pack(q), pack(k), pack(v), pack(g), pack(beta), cu, s_init, threads, lib_path)
+    o = np.swapaxes(o.reshape(B, steps, H, dv), 0, 1)
+    return o, s
