@@ -1,0 +1,147 @@
+/*
+ * gdn.h -- C ABI of the gated delta-rule recurrence library (libgdn.so, gfx950).
+ *
+ * The recurrence, per (sequence, head), with a d_v x d_k fp32 state S:
+ *
+ *     S_t = g_t S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T,      o_t = S_t q_t
+ *
+ * Source: "Qwen3.8-27B 架构深读: Gated DeltaNet 混合线性注意力与 262K 长上下文"
+ * (feifeigd.github.io, 2026-08-17), section 三 (Gated DeltaNet): the gated
+ * delta-rule equation and the single-step sketch (recall with the key from the
+ * ungated state, gate the state, write the correction along the key).  The
+ * read-out o_t = S_t q_t is the page's linear-attention read-out applied to the
+ * updated state.  The same section says training accumulates the state chunk
+ * by chunk in parallel while inference does one fixed-size matrix update per
+ * step: gdn_prefill and gdn_decode_step are those two modes.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the name ends in _host.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it; nothing synchronises and nothing allocates.
+ *   - The caller owns every buffer.  The library keeps no device memory and no
+ *     global state except a per-thread copy of the last error message.
+ *   - Arguments are validated on the host before anything is enqueued.  On any
+ *     error the call returns a non-zero gdn_status, enqueues nothing and leaves
+ *     every output untouched; gdn_last_error() then describes the problem.
+ *     A failing launch returns GDN_ERR_HIP (earlier launches of the same call
+ *     may already be enqueued).
+ *   - Device data is not inspected.  The documented domain is 0 < g <= 1 and
+ *     finite q, k, v, beta and states; g <= 0 is treated as the smallest
+ *     positive float by the chunked prefill.
+ *   - Head dimensions: d_k == d_v, one of 16, 32, 64, 128.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k and v.  g, beta, states and o are always fp32. */
+typedef enum { GDN_BF16 = 0, GDN_FP32 = 1 } gdn_dtype;
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree */
+    GDN_ERR_DTYPE = 3,       /* unknown gdn_dtype */
+    GDN_ERR_ALIGN = 4,       /* q/k/v/o/state not 16-byte aligned, or g/beta not 4-byte aligned */
+    GDN_ERR_SEQLENS = 5,     /* cu_seqlens_host not 0 = c[0] <= c[1] <= ... <= c[n] = total */
+    GDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than gdn_prefill_workspace_bytes() */
+    GDN_ERR_UNSUPPORTED = 7, /* head dimension, dtype or chunk size not built */
+    GDN_ERR_ALIAS = 8,       /* an output overlaps an input it must not overlap */
+    GDN_ERR_HIP = 9          /* the HIP runtime reported an error */
+} gdn_status;
+
+/* Prefill algorithms (the `chunk` argument of gdn_prefill). */
+#define GDN_CHUNK_AUTO 0     /* chunked (64) where built, else token-serial */
+#define GDN_CHUNK_SERIAL 1   /* token-serial: one fixed-size update per token */
+#define GDN_CHUNK_64 64      /* chunkwise-parallel, 64-token chunks, MFMA (bf16 q/k/v, d = 128) */
+
+/* Bytes of fp32 state for n_seq sequences: n_seq * H * dv * dk * 4.
+ * Returns 0 if a size is negative or zero (n_seq == 0 gives 0 as well).
+ * The state is [n_seq][H][dv][dk]: row i of a head's state (its d_k entries)
+ * is contiguous, so each row is one coalesced 4*dk-byte run. */
+size_t gdn_state_bytes(int64_t n_seq, int32_t H, int32_t dk, int32_t dv);
+
+/* Which algorithm gdn_prefill would run for these arguments:
+ * GDN_CHUNK_SERIAL, GDN_CHUNK_64, or 0 if the combination is not supported. */
+int32_t gdn_prefill_algorithm(gdn_dtype dtype, int32_t dk, int32_t dv, int32_t chunk);
+
+/* Set a state before any token arrives ("attention and memory", stethem.com,
+ * "Sources, assumptions & limits": the recurrent state exists before the first
+ * token).  state [n_seq][H][dv][dk] fp32 is written: a copy of `init` (same
+ * layout; may not partially overlap `state`), or zeros when init == NULL. */
+gdn_status gdn_state_init(float *state, int64_t n_seq, int32_t H, int32_t dk, int32_t dv,
+                          const float *init, void *stream);
+
+/* Zero the states of the listed sequences (the batch/reset rule of
+ * "Hybrid · kết hợp nhiều cơ chế..." (openarchlab.com), section 3: a runtime
+ * needs state update and batch/reset rules).  slots: device int32 array of
+ * n_slots sequence indices; entries outside [0, n_seq) are skipped; NULL zeroes
+ * every sequence (n_slots is then ignored). */
+gdn_status gdn_state_reset(float *state, int64_t n_seq, int32_t H, int32_t dk, int32_t dv,
+                           const int32_t *slots, int32_t n_slots, void *stream);
+
+/* Device workspace that gdn_prefill needs for these sizes (0 for the
+ * token-serial algorithm).  Use the same arguments as the gdn_prefill call. */
+size_t gdn_prefill_workspace_bytes(int64_t total_tokens, int64_t n_seq, int32_t H,
+                                   int32_t dk, int32_t dv, gdn_dtype dtype, int32_t chunk);
+
+/* Prefill a packed batch of n_seq sequences (total_tokens tokens in all).
+ *
+ *   q, k          [N][H][dk]  dtype, token-major, contiguous, 16-byte aligned
+ *   v             [N][H][dv]  dtype
+ *   g, beta       [N][H]      fp32 (gate and write strength per token and head)
+ *   cu_seqlens    [n_seq+1]   int32 device copy of the sequence offsets, and
+ *   cu_seqlens_host           the same offsets in host memory (validated here);
+ *                             both NULL means one sequence (n_seq must be 1)
+ *   initial_state [n_seq][H][dv][dk] fp32, or NULL for zeros.  May be the same
+ *                             pointer as final_state (updated in place), but may
+ *                             not otherwise overlap it.
+ *   o             [N][H][dv]  fp32 output (must not overlap any input)
+ *   final_state   [n_seq][H][dv][dk] fp32 output
+ *   chunk         GDN_CHUNK_AUTO, GDN_CHUNK_SERIAL or GDN_CHUNK_64
+ *   workspace     device scratch of at least gdn_prefill_workspace_bytes();
+ *                 may be NULL when that is 0.  Its contents on entry do not matter.
+ *
+ * Each sequence starts from its own initial state and never sees another
+ * sequence's tokens; a zero-length sequence copies its initial state to its
+ * final state.  Running a sequence in segments, feeding each final state back
+ * as the next initial state, gives the one-shot result up to rounding
+ * ("Hybrid..." (openarchlab.com), section 4: segmented runs with carried state
+ * must not change the result). */
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dtype,
+                       const float *g, const float *beta,
+                       const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
+                       int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                       const float *initial_state, float *o, float *final_state,
+                       int32_t chunk, void *workspace, size_t workspace_bytes, void *stream);
+
+/* One token for each of B sequences, updating their states in place.
+ *
+ *   q, k    [B][H][dk] dtype;   v [B][H][dv] dtype;   g, beta [B][H] fp32
+ *   state   [B][H][dv][dk] fp32, read once and written once (in place)
+ *   o       [B][H][dv] fp32, o = S_t q_t from the updated state
+ *
+ * The per-token cost is fixed, whatever the position of the token ("Layouts
+ * híbridos: três DeltaNet, uma attention" (llmdeepdive.com), section Conceito:
+ * the state is a fixed set of matrices edited in place). */
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtype dtype,
+                           const float *g, const float *beta, float *state, float *o,
+                           int64_t B, int32_t H, int32_t dk, int32_t dv, void *stream);
+
+/* Static description of a status code. */
+const char *gdn_status_string(gdn_status status);
+
+/* Detail of the last failing call made by the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,7 @@
+"""MI355X-native gated delta-rule recurrence (Gated DeltaNet mixer core).
+
+The compute lives in libgdn.so (hand-written HIP for gfx950, C ABI in
+include/gdn.h); ``gdn`` is its thin Python binding.
+"""
+from .gdn import (GdnError, decode_step, prefill, prefill_algorithm, prefill_workspace_bytes,  # noqa: F401
+                  state_bytes, state_init, state_reset)

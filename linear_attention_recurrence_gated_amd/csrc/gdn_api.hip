@@ -1,0 +1,253 @@
+// gdn_api.hip -- the C ABI declared in include/gdn.h: host-side validation,
+// algorithm choice and launches.  Nothing here allocates device memory or
+// synchronises; every launch goes on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+gdn_status ok() {
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+gdn_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_d(int32_t dk, int32_t dv) {
+    return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
+
+struct Range {
+    const void *p;
+    size_t n;
+};
+
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// 0 = unsupported; otherwise the algorithm gdn_prefill runs.
+int32_t pick_algorithm(gdn_dtype dtype, int32_t dk, int32_t dv, int32_t chunk) {
+    if (dtype != GDN_BF16 && dtype != GDN_FP32) return 0;
+    if (!supported_d(dk, dv)) return 0;
+    const bool chunked_built = false && dtype == GDN_BF16 && dk == 128;
+    switch (chunk) {
+        case GDN_CHUNK_AUTO: return chunked_built ? GDN_CHUNK_64 : GDN_CHUNK_SERIAL;
+        case GDN_CHUNK_SERIAL: return GDN_CHUNK_SERIAL;
+        case GDN_CHUNK_64: return chunked_built ? GDN_CHUNK_64 : 0;
+        default: return 0;
+    }
+}
+
+// Multiplication with an overflow check against SIZE_MAX / 2.
+bool mul_ok(size_t a, size_t b, size_t *out) {
+    if (a != 0 && b > (SIZE_MAX / 2) / a) return false;
+    *out = a * b;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_state_bytes(int64_t n_seq, int32_t H, int32_t dk, int32_t dv) {
+    if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0) return 0;
+    size_t a, b, c;
+    if (!mul_ok((size_t)n_seq, (size_t)H, &a) || !mul_ok(a, (size_t)dk * (size_t)dv, &b) || !mul_ok(b, 4, &c))
+        return 0;
+    return c;
+}
+
+int32_t gdn_prefill_algorithm(gdn_dtype dtype, int32_t dk, int32_t dv, int32_t chunk) {
+    return pick_algorithm(dtype, dk, dv, chunk);
+}
+
+const char *gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "null pointer";
+        case GDN_ERR_SHAPE: return "invalid size";
+        case GDN_ERR_DTYPE: return "invalid dtype";
+        case GDN_ERR_ALIGN: return "misaligned pointer";
+        case GDN_ERR_SEQLENS: return "invalid cu_seqlens";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case GDN_ERR_ALIAS: return "overlapping buffers";
+        case GDN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *gdn_last_error(void) { return g_last_error.c_str(); }
+
+gdn_status gdn_state_init(float *state, int64_t n_seq, int32_t H, int32_t dk, int32_t dv, const float *init,
+                          void *stream) {
+    if (n_seq < 0 || H <= 0) return fail(GDN_ERR_SHAPE, "state_init: n_seq=%lld H=%d", (long long)n_seq, H);
+    if (!supported_d(dk, dv)) return fail(GDN_ERR_UNSUPPORTED, "state_init: dk=%d dv=%d not supported", dk, dv);
+    const size_t bytes = gdn_state_bytes(n_seq, H, dk, dv);
+    if (bytes == 0) return ok();
+    if (!state) return fail(GDN_ERR_NULL, "state_init: state is NULL");
+    if (!aligned(state, 16) || (init && !aligned(init, 16)))
+        return fail(GDN_ERR_ALIGN, "state_init: state/init must be 16-byte aligned");
+    if (init && init != state && overlap({state, bytes}, {init, bytes}))
+        return fail(GDN_ERR_ALIAS, "state_init: init partially overlaps state");
+    return hip_status(gdn::launch_state_fill(state, init, (int64_t)(bytes / 4), (hipStream_t)stream),
+                      "state_init launch");
+}
+
+gdn_status gdn_state_reset(float *state, int64_t n_seq, int32_t H, int32_t dk, int32_t dv, const int32_t *slots,
+                           int32_t n_slots, void *stream) {
+    if (n_seq < 0 || H <= 0) return fail(GDN_ERR_SHAPE, "state_reset: n_seq=%lld H=%d", (long long)n_seq, H);
+    if (!supported_d(dk, dv)) return fail(GDN_ERR_UNSUPPORTED, "state_reset: dk=%d dv=%d not supported", dk, dv);
+    if (slots && (n_slots < 0 || n_slots > 65535))
+        return fail(GDN_ERR_SHAPE, "state_reset: n_slots=%d outside [0, 65535]", n_slots);
+    const size_t bytes = gdn_state_bytes(n_seq, H, dk, dv);
+    if (bytes == 0) return ok();
+    if (!state) return fail(GDN_ERR_NULL, "state_reset: state is NULL");
+    if (!aligned(state, 16)) return fail(GDN_ERR_ALIGN, "state_reset: state must be 16-byte aligned");
+    if (slots && !aligned(slots, 4)) return fail(GDN_ERR_ALIGN, "state_reset: slots must be 4-byte aligned");
+    hipError_t e;
+    if (!slots) {
+        e = gdn::launch_state_fill(state, nullptr, (int64_t)(bytes / 4), (hipStream_t)stream);
+    } else {
+        e = gdn::launch_state_reset_slots(state, slots, n_slots, n_seq, (int64_t)H * dk * dv, (hipStream_t)stream);
+    }
+    return hip_status(e, "state_reset launch");
+}
+
+size_t gdn_prefill_workspace_bytes(int64_t total_tokens, int64_t n_seq, int32_t H, int32_t dk, int32_t dv,
+                                   gdn_dtype dtype, int32_t chunk) {
+    if (total_tokens < 0 || n_seq < 0 || H <= 0) return 0;
+    if (pick_algorithm(dtype, dk, dv, chunk) != GDN_CHUNK_64) return 0;
+    return gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H);
+}
+
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dtype, const float *g,
+                       const float *beta, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
+                       int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, const float *initial_state,
+                       float *o, float *final_state, int32_t chunk, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    if (dtype != GDN_BF16 && dtype != GDN_FP32) return fail(GDN_ERR_DTYPE, "prefill: dtype %d", (int)dtype);
+    if (n_seq < 0 || total_tokens < 0 || H <= 0 || total_tokens > (int64_t)INT32_MAX)
+        return fail(GDN_ERR_SHAPE, "prefill: n_seq=%lld total_tokens=%lld H=%d", (long long)n_seq,
+                    (long long)total_tokens, H);
+    const int32_t algo = pick_algorithm(dtype, dk, dv, chunk);
+    if (!algo)
+        return fail(GDN_ERR_UNSUPPORTED, "prefill: dtype=%d dk=%d dv=%d chunk=%d not supported", (int)dtype, dk, dv,
+                    chunk);
+    // sequence offsets
+    if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr))
+        return fail(GDN_ERR_NULL, "prefill: cu_seqlens and cu_seqlens_host must both be given or both be NULL");
+    if (!cu_seqlens) {
+        if (n_seq != 1) return fail(GDN_ERR_SEQLENS, "prefill: without cu_seqlens n_seq must be 1 (got %lld)",
+                                    (long long)n_seq);
+    } else {
+        if (!aligned(cu_seqlens, 4)) return fail(GDN_ERR_ALIGN, "prefill: cu_seqlens must be 4-byte aligned");
+        if (cu_seqlens_host[0] != 0) return fail(GDN_ERR_SEQLENS, "prefill: cu_seqlens[0] = %d", cu_seqlens_host[0]);
+        for (int64_t s = 0; s < n_seq; ++s)
+            if (cu_seqlens_host[s + 1] < cu_seqlens_host[s])
+                return fail(GDN_ERR_SEQLENS, "prefill: cu_seqlens decreases at %lld", (long long)s);
+        if ((int64_t)cu_seqlens_host[n_seq] != total_tokens)
+            return fail(GDN_ERR_SEQLENS, "prefill: cu_seqlens[n_seq] = %d but total_tokens = %lld",
+                        cu_seqlens_host[n_seq], (long long)total_tokens);
+    }
+    const size_t sbytes = gdn_state_bytes(n_seq, H, dk, dv);
+    if (n_seq > 0 && sbytes == 0) return fail(GDN_ERR_SHAPE, "prefill: state size overflows");
+    if (n_seq > 0 && !final_state) return fail(GDN_ERR_NULL, "prefill: final_state is NULL");
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
+        return fail(GDN_ERR_NULL, "prefill: q, k, v, g, beta and o are required when total_tokens > 0");
+    const size_t eb = elem_bytes(dtype);
+    const size_t N = (size_t)total_tokens;
+    const size_t qk_bytes = N * H * dk * eb, v_bytes = N * H * dv * eb, gb_bytes = N * H * 4,
+                 o_bytes = N * H * dv * 4;
+    if (total_tokens > 0) {
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+            return fail(GDN_ERR_ALIGN, "prefill: q, k, v and o must be 16-byte aligned");
+        if (!aligned(g, 4) || !aligned(beta, 4)) return fail(GDN_ERR_ALIGN, "prefill: g, beta must be 4-byte aligned");
+    }
+    if ((final_state && !aligned(final_state, 16)) || (initial_state && !aligned(initial_state, 16)))
+        return fail(GDN_ERR_ALIGN, "prefill: states must be 16-byte aligned");
+    // aliasing: o and final_state are outputs; initial_state may equal final_state exactly
+    const Range rq{q, qk_bytes}, rk{k, qk_bytes}, rv{v, v_bytes}, rg{g, gb_bytes}, rb{beta, gb_bytes},
+        ro{o, o_bytes}, rs0{initial_state, initial_state ? sbytes : 0}, rs1{final_state, sbytes},
+        rcu{cu_seqlens, cu_seqlens ? (size_t)(n_seq + 1) * 4 : 0};
+    for (Range in : {rq, rk, rv, rg, rb, rs0, rcu, rs1})
+        if (overlap(ro, in)) return fail(GDN_ERR_ALIAS, "prefill: o overlaps another argument");
+    for (Range in : {rq, rk, rv, rg, rb, rcu})
+        if (overlap(rs1, in)) return fail(GDN_ERR_ALIAS, "prefill: final_state overlaps an input");
+    if (initial_state && initial_state != final_state && overlap(rs0, rs1))
+        return fail(GDN_ERR_ALIAS, "prefill: initial_state partially overlaps final_state");
+
+    hipStream_t st = (hipStream_t)stream;
+    if (n_seq == 0) return ok();
+    if (algo == GDN_CHUNK_64) {
+        const size_t need = gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H);
+        if (need > 0 && (!workspace || workspace_bytes < need))
+            return fail(GDN_ERR_WORKSPACE, "prefill: workspace of %zu bytes needed, %zu given", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (workspace && !aligned(workspace, 256)) return fail(GDN_ERR_ALIGN, "prefill: workspace must be 256-byte aligned");
+        for (Range in : {rq, rk, rv, rg, rb, rs0, rcu, ro, rs1})
+            if (overlap({workspace, need}, in)) return fail(GDN_ERR_ALIAS, "prefill: workspace overlaps an argument");
+        return hip_status(gdn::launch_prefill_chunked(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, n_seq,
+                                                      total_tokens, H, initial_state, o, final_state, workspace, st),
+                          "prefill (chunked) launch");
+    }
+    return hip_status(gdn::launch_prefill_serial(dtype == GDN_BF16, dk, q, k, v, g, beta, cu_seqlens, n_seq,
+                                                 total_tokens, H, initial_state, o, final_state, st),
+                      "prefill (serial) launch");
+}
+
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtype dtype, const float *g,
+                           const float *beta, float *state, float *o, int64_t B, int32_t H, int32_t dk, int32_t dv,
+                           void *stream) {
+    if (dtype != GDN_BF16 && dtype != GDN_FP32) return fail(GDN_ERR_DTYPE, "decode_step: dtype %d", (int)dtype);
+    if (B < 0 || H <= 0 || B * (int64_t)H > (int64_t)UINT32_MAX)
+        return fail(GDN_ERR_SHAPE, "decode_step: B=%lld H=%d", (long long)B, H);
+    if (!supported_d(dk, dv)) return fail(GDN_ERR_UNSUPPORTED, "decode_step: dk=%d dv=%d not supported", dk, dv);
+    if (B == 0) return ok();
+    if (!q || !k || !v || !g || !beta || !state || !o)
+        return fail(GDN_ERR_NULL, "decode_step: every pointer is required");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16) || !aligned(o, 16))
+        return fail(GDN_ERR_ALIGN, "decode_step: q, k, v, state and o must be 16-byte aligned");
+    if (!aligned(g, 4) || !aligned(beta, 4)) return fail(GDN_ERR_ALIGN, "decode_step: g, beta must be 4-byte aligned");
+    const size_t eb = elem_bytes(dtype), BH = (size_t)B * H;
+    const Range rq{q, BH * dk * eb}, rk{k, BH * dk * eb}, rv{v, BH * dv * eb}, rg{g, BH * 4}, rb{beta, BH * 4},
+        rs{state, gdn_state_bytes(B, H, dk, dv)}, ro{o, BH * dv * 4};
+    for (Range in : {rq, rk, rv, rg, rb, rs})
+        if (overlap(ro, in)) return fail(GDN_ERR_ALIAS, "decode_step: o overlaps another argument");
+    for (Range in : {rq, rk, rv, rg, rb})
+        if (overlap(rs, in)) return fail(GDN_ERR_ALIAS, "decode_step: state overlaps an input");
+    return hip_status(gdn::launch_decode(dtype == GDN_BF16, dk, q, k, v, g, beta, state, o, (int64_t)BH,
+                                         (hipStream_t)stream),
+                      "decode_step launch");
+}
+
+}  // extern "C"

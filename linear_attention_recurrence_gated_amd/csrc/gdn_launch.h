@@ -1,0 +1,40 @@
+// gdn_launch.h -- host-side launchers of the device kernels (internal).
+//
+// Arguments are already validated by gdn_api.hip; each launcher only enqueues
+// its kernel(s) on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// One decode step for B*H heads (in-place state update).
+hipError_t launch_decode(bool bf16, int d, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, float *state, float *o,
+                         int64_t BH, hipStream_t stream);
+
+// Token-serial prefill: one workgroup per (sequence, head, row tile) walks the
+// sequence's tokens in order.
+hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta, const int32_t *cu_seqlens,
+                                 int64_t n_seq, int64_t total_tokens, int H,
+                                 const float *initial_state, float *o, float *final_state,
+                                 hipStream_t stream);
+
+// Chunkwise-parallel prefill (64-token chunks, d = 128, bf16 q/k/v).
+size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H);
+hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta, const int32_t *cu_seqlens,
+                                  const int32_t *cu_seqlens_host, int64_t n_seq,
+                                  int64_t total_tokens, int H, const float *initial_state,
+                                  float *o, float *final_state, void *workspace,
+                                  hipStream_t stream);
+
+// state[0 : n_floats] = init ? init : 0
+hipError_t launch_state_fill(float *state, const float *init, int64_t n_floats, hipStream_t stream);
+// zero blocks slots[i] (each block_floats long) for 0 <= slots[i] < n_blocks
+hipError_t launch_state_reset_slots(float *state, const int32_t *slots, int32_t n_slots,
+                                    int64_t n_blocks, int64_t block_floats, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,230 @@
+// gdn_rowstream.hip -- the two token-at-a-time kernels of the gated delta rule.
+//
+// Both follow the single-step update of "Qwen3.8-27B 架构深读" (feifeigd.github.io,
+// 2026-08-17), section 三 (Gated DeltaNet): recall S k from the state before the
+// gate, decay the state by g, write beta (v - recall) k^T.  The read-out uses
+//     o_t = S_t q_t = g_t (S_{t-1} q_t) + c_t (k_t . q_t),   c_t = beta_t (v_t - S_{t-1} k_t),
+// so one read of each state row yields everything: two dot products (with k and
+// with q) and the rank-one update.
+//
+// Layout: the state of one head is d_v rows of d_k fp32, each row contiguous.
+// A row is split over LPR = d/8 lanes; lane r of a row holds columns
+// [4r, 4r+4) and [d/2 + 4r, d/2 + 4r + 4), so every float4 load of the wave
+// touches contiguous 16-byte runs and a row's two dot products finish with an
+// LPR-lane DPP reduction.  Rows are independent: row i only needs v[i], its own
+// previous values and the shared k, q, g, beta.
+//
+//   k_decode_step   one step for B*H heads; a workgroup owns one head's whole
+//                   state, reads it once and writes it once (HBM-bound).
+//   k_prefill_serial  one workgroup per (sequence, head, row tile) walks the
+//                   sequence token by token with its rows held in registers.
+//                   Used for fp32 inputs and head sizes without a chunked
+//                   kernel, and as an independent GPU cross-check.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+template <int D>
+struct RowLayout {
+    static constexpr int LPR = D / 8;    // lanes per state row
+    static constexpr int RPP = 64 / LPR; // rows per wave pass
+};
+
+// ---------------------------------------------------------------------------
+// Decode: grid = B*H workgroups of NW waves; wave w owns rows [w*D/NW, (w+1)*D/NW).
+template <typename TIn, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__ q, const TIn *__restrict__ k,
+                                                         const TIn *__restrict__ v, const float *__restrict__ g,
+                                                         const float *__restrict__ beta, float *__restrict__ state,
+                                                         float *__restrict__ o) {
+    using L = RowLayout<D>;
+    constexpr int RPW = D / NW;
+    constexpr int PASSES = (RPW + L::RPP - 1) / L::RPP;
+    const int64_t bh = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane % L::LPR, rs = lane / L::LPR;
+    const int c0 = 4 * lr, c1 = D / 2 + 4 * lr;
+
+    const TIn *kp = k + bh * D;
+    const TIn *qp = q + bh * D;
+    const float4 k0 = In<TIn>::load4(kp + c0), k1 = In<TIn>::load4(kp + c1);
+    const float4 q0 = In<TIn>::load4(qp + c0), q1 = In<TIn>::load4(qp + c1);
+    const float gt = g[bh], bt = beta[bh];
+    float *S = state + bh * (int64_t)D * D;
+
+    float4 s0[PASSES], s1[PASSES];
+    float vr[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int rloc = p * L::RPP + rs;
+        const bool ok = rloc < RPW;
+        const int row = wave * RPW + (ok ? rloc : 0);
+        if (ok) {
+            s0[p] = *reinterpret_cast<const float4 *>(S + row * D + c0);
+            s1[p] = *reinterpret_cast<const float4 *>(S + row * D + c1);
+        } else {
+            s0[p] = s1[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        vr[p] = In<TIn>::load1(v + bh * D + row);
+    }
+    const float kq = group_sum<L::LPR>(dot4(k0, q0) + dot4(k1, q1));
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int rloc = p * L::RPP + rs;
+        const bool ok = rloc < RPW;
+        const int row = wave * RPW + rloc;
+        const float a = group_sum<L::LPR>(dot4(s0[p], k0) + dot4(s1[p], k1));
+        const float b = group_sum<L::LPR>(dot4(s0[p], q0) + dot4(s1[p], q1));
+        const float c = bt * (vr[p] - a);
+        if (ok) {
+            *reinterpret_cast<float4 *>(S + row * D + c0) = axpby4(gt, s0[p], c, k0);
+            *reinterpret_cast<float4 *>(S + row * D + c1) = axpby4(gt, s1[p], c, k1);
+            if (lr == 0) o[bh * D + row] = gt * b + c * kq;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Token-serial prefill: grid = n_seq * H * (D / ROWS) single-wave workgroups.
+template <typename TIn, int D, int ROWS>
+__global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q, const TIn *__restrict__ k,
+                                                       const TIn *__restrict__ v, const float *__restrict__ g,
+                                                       const float *__restrict__ beta,
+                                                       const int32_t *__restrict__ cu_seqlens, int64_t total_tokens,
+                                                       int H, const float *initial_state, float *__restrict__ o,
+                                                       float *final_state) {
+    using L = RowLayout<D>;
+    constexpr int TILES = D / ROWS;
+    constexpr int PASSES = (ROWS + L::RPP - 1) / L::RPP;
+    const int64_t blk = blockIdx.x;
+    const int tile = int(blk % TILES);
+    const int64_t sh = blk / TILES;
+    const int h = int(sh % H);
+    const int64_t s = sh / H;
+    const int lane = threadIdx.x;
+    const int lr = lane % L::LPR, rs = lane / L::LPR;
+    const int c0 = 4 * lr, c1 = D / 2 + 4 * lr;
+    const int64_t t0 = cu_seqlens ? cu_seqlens[s] : 0;
+    const int64_t t1 = cu_seqlens ? cu_seqlens[s + 1] : total_tokens;
+
+    const int64_t sbase = sh * (int64_t)D * D;
+    float4 s0[PASSES], s1[PASSES];
+    int rowp[PASSES];
+    bool okp[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int rloc = p * L::RPP + rs;
+        okp[p] = rloc < ROWS;
+        rowp[p] = tile * ROWS + (okp[p] ? rloc : 0);
+        s0[p] = s1[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (initial_state && okp[p]) {
+            s0[p] = *reinterpret_cast<const float4 *>(initial_state + sbase + rowp[p] * D + c0);
+            s1[p] = *reinterpret_cast<const float4 *>(initial_state + sbase + rowp[p] * D + c1);
+        }
+    }
+
+    // one-token lookahead on the per-token inputs
+    float4 k0n, k1n, q0n, q1n;
+    float vn[PASSES], gn = 1.f, bn = 0.f;
+    auto fetch = [&](int64_t t) {
+        const int64_t th = t * H + h;
+        k0n = In<TIn>::load4(k + th * D + c0);
+        k1n = In<TIn>::load4(k + th * D + c1);
+        q0n = In<TIn>::load4(q + th * D + c0);
+        q1n = In<TIn>::load4(q + th * D + c1);
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) vn[p] = In<TIn>::load1(v + th * D + rowp[p]);
+        gn = g[th];
+        bn = beta[th];
+    };
+    if (t0 < t1) fetch(t0);
+    for (int64_t t = t0; t < t1; ++t) {
+        const float4 k0 = k0n, k1 = k1n, q0 = q0n, q1 = q1n;
+        float vr[PASSES];
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) vr[p] = vn[p];
+        const float gt = gn, bt = bn;
+        if (t + 1 < t1) fetch(t + 1);
+        const float kq = group_sum<L::LPR>(dot4(k0, q0) + dot4(k1, q1));
+        float* orow = o + (t * H + h) * (int64_t)D;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const float a = group_sum<L::LPR>(dot4(s0[p], k0) + dot4(s1[p], k1));
+            const float b = group_sum<L::LPR>(dot4(s0[p], q0) + dot4(s1[p], q1));
+            const float c = bt * (vr[p] - a);
+            s0[p] = axpby4(gt, s0[p], c, k0);
+            s1[p] = axpby4(gt, s1[p], c, k1);
+            if (okp[p] && lr == 0) orow[rowp[p]] = gt * b + c * kq;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        if (okp[p]) {
+            *reinterpret_cast<float4 *>(final_state + sbase + rowp[p] * D + c0) = s0[p];
+            *reinterpret_cast<float4 *>(final_state + sbase + rowp[p] * D + c1) = s1[p];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+
+template <typename TIn, int D>
+static hipError_t decode_d(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                           float *state, float *o, int64_t BH, hipStream_t stream) {
+    constexpr int NW = D >= 64 ? 4 : 1;
+    hipLaunchKernelGGL((k_decode_step<TIn, D, NW>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
+                       (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(bool bf16, int d, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, float *state, float *o, int64_t BH, hipStream_t stream) {
+    if (BH == 0) return hipSuccess;
+#define GDN_DEC(D)                                                                          \
+    case D:                                                                                 \
+        return bf16 ? decode_d<uint16_t, D>(q, k, v, g, beta, state, o, BH, stream)         \
+                    : decode_d<float, D>(q, k, v, g, beta, state, o, BH, stream);
+    switch (d) {
+        GDN_DEC(16)
+        GDN_DEC(32)
+        GDN_DEC(64)
+        GDN_DEC(128)
+    }
+#undef GDN_DEC
+    return hipErrorInvalidValue;
+}
+
+template <typename TIn, int D>
+static hipError_t serial_d(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                           const int32_t *cu, int64_t n_seq, int64_t total, int H, const float *s_in, float *o,
+                           float *s_out, hipStream_t stream) {
+    constexpr int ROWS = D >= 32 ? 32 : D;
+    const int64_t blocks = n_seq * H * (D / ROWS);
+    hipLaunchKernelGGL((k_prefill_serial<TIn, D, ROWS>), dim3((unsigned)blocks), dim3(64), 0, stream,
+                       (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, cu, total, H, s_in, o, s_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const int32_t *cu_seqlens, int64_t n_seq,
+                                 int64_t total_tokens, int H, const float *initial_state, float *o,
+                                 float *final_state, hipStream_t stream) {
+    if (n_seq == 0) return hipSuccess;
+#define GDN_SER(D)                                                                                         \
+    case D:                                                                                                \
+        return bf16 ? serial_d<uint16_t, D>(q, k, v, g, beta, cu_seqlens, n_seq, total_tokens, H,         \
+                                            initial_state, o, final_state, stream)                         \
+                    : serial_d<float, D>(q, k, v, g, beta, cu_seqlens, n_seq, total_tokens, H,            \
+                                         initial_state, o, final_state, stream);
+    switch (d) {
+        GDN_SER(16)
+        GDN_SER(32)
+        GDN_SER(64)
+        GDN_SER(128)
+    }
+#undef GDN_SER
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

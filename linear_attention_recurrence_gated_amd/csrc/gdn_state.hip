@@ -1,0 +1,55 @@
+// gdn_state.hip -- set and reset recurrent states.
+//
+// The state exists before the first token ("attention and memory",
+// stethem.com, "Sources, assumptions & limits"), and a runtime needs batch and
+// reset rules for it ("Hybrid · kết hợp nhiều cơ chế..." (openarchlab.com),
+// section 3).  Both kernels are plain grid-stride float4 streams.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+__global__ __launch_bounds__(256) void k_state_fill(float4 *__restrict__ dst, const float4 *__restrict__ src,
+                                                    int64_t n4) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// grid.y walks the slot list; grid.x strides over one state block.
+__global__ __launch_bounds__(256) void k_state_reset_slots(float4 *__restrict__ state,
+                                                           const int32_t *__restrict__ slots, int64_t n_blocks,
+                                                           int64_t block4) {
+    const int32_t s = slots[blockIdx.y];
+    if (s < 0 || s >= n_blocks) return;
+    float4 *dst = state + (int64_t)s * block4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < block4; i += stride)
+        dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+static unsigned grid_for(int64_t n4) {
+    const int64_t want = (n4 + 255) / 256;
+    return (unsigned)(want < 8192 ? (want > 0 ? want : 1) : 8192);
+}
+
+hipError_t launch_state_fill(float *state, const float *init, int64_t n_floats, hipStream_t stream) {
+    if (n_floats == 0 || init == state) return hipSuccess;
+    const int64_t n4 = n_floats / 4;  // every supported state block is a multiple of 16 floats
+    hipLaunchKernelGGL(k_state_fill, dim3(grid_for(n4)), dim3(256), 0, stream, (float4 *)state,
+                       (const float4 *)init, n4);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_reset_slots(float *state, const int32_t *slots, int32_t n_slots, int64_t n_blocks,
+                                    int64_t block_floats, hipStream_t stream) {
+    if (n_slots == 0 || n_blocks == 0) return hipSuccess;
+    const int64_t block4 = block_floats / 4;
+    int64_t gx = (block4 + 255) / 256;
+    if (gx > 1024) gx = 1024;
+    hipLaunchKernelGGL(k_state_reset_slots, dim3((unsigned)gx, (unsigned)n_slots), dim3(256), 0, stream,
+                       (float4 *)state, slots, n_blocks, block4);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

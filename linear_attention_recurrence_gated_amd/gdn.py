@@ -1,0 +1,196 @@
+"""Python binding of libgdn.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels.  PyTorch only provides
+device memory and the current stream.  There is no fallback: if libgdn.so is
+missing or fails to load, every call raises.
+
+Names mirror include/gdn.h:
+    prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=0) -> (o, final_state)
+    decode_step(q, k, v, g, beta, state) -> o          (state updated in place)
+    state_init(state, init=None), state_reset(state, slots=None)
+    state_bytes(...), prefill_workspace_bytes(...), prefill_algorithm(...)
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+GDN_BF16, GDN_FP32 = 0, 1
+CHUNK_AUTO, CHUNK_SERIAL, CHUNK_64 = 0, 1, 64
+
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
+          5: "GDN_ERR_SEQLENS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_UNSUPPORTED", 8: "GDN_ERR_ALIAS",
+          9: "GDN_ERR_HIP"}
+
+# Every symbol include/gdn.h declares, with (restype, argtypes).
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "gdn_state_bytes": (_sz, [_i64, _i32, _i32, _i32]),
+    "gdn_prefill_algorithm": (_i32, [_i32, _i32, _i32, _i32]),
+    "gdn_state_init": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp]),
+    "gdn_state_reset": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "gdn_prefill_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32, _i32, _i32]),
+    "gdn_prefill": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32,
+                           _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "gdn_decode_step": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "gdn_status_string": (ctypes.c_char_p, [_i32]),
+    "gdn_last_error": (ctypes.c_char_p, []),
+}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        self.detail = detail
+        super().__init__(f"{self.name}: {detail}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libgdn.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m linear_attention_recurrence_gated_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        L = lib()
+        raise GdnError(status, L.gdn_last_error().decode(errors="replace"))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_FP32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(device, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def state_bytes(n_seq, H, dk, dv):
+    return int(lib().gdn_state_bytes(n_seq, H, dk, dv))
+
+
+def prefill_algorithm(dtype_code, dk, dv, chunk=CHUNK_AUTO):
+    return int(lib().gdn_prefill_algorithm(dtype_code, dk, dv, chunk))
+
+
+def prefill_workspace_bytes(total_tokens, n_seq, H, dk, dv, dtype_code=GDN_BF16, chunk=CHUNK_AUTO):
+    return int(lib().gdn_prefill_workspace_bytes(total_tokens, n_seq, H, dk, dv, dtype_code, chunk))
+
+
+def state_init(state, init=None, stream=None):
+    """Set state [n, H, dv, dk] (fp32) to a copy of `init`, or to zeros."""
+    import torch
+    n, H, dv, dk = state.shape
+    _check(lib().gdn_state_init(_dev_ptr(state, "state", torch.float32), n, H, dk, dv,
+                                _dev_ptr(init, "init", torch.float32), _stream(state.device, stream)))
+    return state
+
+
+def state_reset(state, slots=None, stream=None):
+    """Zero the states of the sequences listed in `slots` (device int32), or all."""
+    import torch
+    n, H, dv, dk = state.shape
+    n_slots = 0 if slots is None else slots.numel()
+    _check(lib().gdn_state_reset(_dev_ptr(state, "state", torch.float32), n, H, dk, dv,
+                                 _dev_ptr(slots, "slots", torch.int32), n_slots, _stream(state.device, stream)))
+    return state
+
+
+def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=CHUNK_AUTO,
+            cu_seqlens_device=None, out=None, final_state=None, workspace=None, stream=None):
+    """Chunkwise (or token-serial) prefill of a packed batch.
+
+    q, k: [N, H, dk]; v: [N, H, dv] (bf16 or fp32, device); g, beta: [N, H] fp32.
+    cu_seqlens: host offsets (list, numpy or CPU tensor) of the packed sequences,
+    or None for one sequence; cu_seqlens_device: optional device int32 copy.
+    initial_state: [n_seq, H, dv, dk] fp32 or None (zeros); it may be the same
+    tensor as final_state.  Returns (o [N, H, dv] fp32, final_state).
+    """
+    import torch
+    N, H, dk = k.shape
+    dv = v.shape[2]
+    dev = k.device
+    if cu_seqlens is None:
+        n_seq, cu_host, cu_dev = 1, None, None
+    else:
+        cu_host = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if torch.is_tensor(cu_seqlens) else cu_seqlens,
+                                                  dtype=np.int32))
+        n_seq = cu_host.shape[0] - 1
+        cu_dev = cu_seqlens_device
+        if cu_dev is None:
+            cu_dev = torch.from_numpy(cu_host).to(dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    if final_state is None:
+        final_state = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=dev)
+    code = _dtype_code(k)
+    for name, t in (("q", q), ("v", v)):
+        if t.dtype != k.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from k dtype {k.dtype}")
+    ws_bytes = prefill_workspace_bytes(N, n_seq, H, dk, dv, code, chunk)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_ptr = _dev_ptr(workspace, "workspace") if ws_bytes else None
+    ws_len = workspace.numel() * workspace.element_size() if (ws_bytes and workspace is not None) else 0
+    cu_host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    _check(lib().gdn_prefill(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), code,
+        _dev_ptr(g, "g", torch.float32), _dev_ptr(beta, "beta", torch.float32),
+        _dev_ptr(cu_dev, "cu_seqlens_device", torch.int32), cu_host_ptr, n_seq, N, H, dk, dv,
+        _dev_ptr(initial_state, "initial_state", torch.float32),
+        _dev_ptr(out, "out", torch.float32), _dev_ptr(final_state, "final_state", torch.float32),
+        chunk, ws_ptr, ws_len, _stream(dev, stream)))
+    return out, final_state
+
+
+def decode_step(q, k, v, g, beta, state, out=None, stream=None):
+    """One token per sequence: q, k [B, H, dk], v [B, H, dv], g, beta [B, H];
+    state [B, H, dv, dk] fp32 updated in place.  Returns o [B, H, dv] fp32."""
+    import torch
+    B, H, dk = k.shape
+    dv = v.shape[2]
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=torch.float32, device=k.device)
+    _check(lib().gdn_decode_step(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k),
+        _dev_ptr(g, "g", torch.float32), _dev_ptr(beta, "beta", torch.float32),
+        _dev_ptr(state, "state", torch.float32), _dev_ptr(out, "out", torch.float32),
+        B, H, dk, dv, _stream(k.device, stream)))
+    return out

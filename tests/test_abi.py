@@ -1,0 +1,162 @@
+"""The C ABI without a GPU: symbols, sizes and host-side validation.
+
+Every call here fails validation on the host, so nothing is ever enqueued
+(the pointers passed are never dereferenced).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from linear_attention_recurrence_gated_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["gdn_prefill", "gdn_decode_step", "gdn_state_init", "gdn_state_reset",
+                 "gdn_state_bytes", "gdn_prefill_workspace_bytes", "gdn_status_string", "gdn_last_error",
+                 "gdn_prefill_algorithm"]:
+        assert want in names
+    assert set(names) == set(gdn.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_library_exports_every_declared_symbol():
+    L = gdn.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (gdn_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_state_bytes_reproduces_the_pages_144_mib():
+    vals = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "state_memory.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            k, v = (x.strip() for x in line.split("="))
+            vals[k] = int(v)
+    per_layer = gdn.state_bytes(1, vals["heads"], vals["dk"], vals["dv"])
+    assert per_layer * vals["layers"] == vals["total_bytes"] == 144 * 2 ** 20
+    # no length argument at all: the state does not grow with context
+    assert gdn.state_bytes(64, 48, 128, 128) == 64 * per_layer
+    assert gdn.state_bytes(-1, 48, 128, 128) == 0 and gdn.state_bytes(1, 0, 128, 128) == 0
+
+
+def test_status_strings():
+    L = gdn.lib()
+    for code, name in gdn.STATUS.items():
+        assert L.gdn_status_string(code)
+    assert L.gdn_status_string(12345) == b"unknown status"
+
+
+def test_algorithm_choice():
+    A = gdn.prefill_algorithm
+    assert A(gdn.GDN_FP32, 16, 16, 0) == gdn.CHUNK_SERIAL
+    assert A(gdn.GDN_FP32, 128, 128, gdn.CHUNK_64) == 0
+    assert A(gdn.GDN_BF16, 100, 100, 0) == 0
+    assert A(gdn.GDN_BF16, 128, 64, 0) == 0
+    assert A(7, 128, 128, 0) == 0
+    assert A(gdn.GDN_BF16, 128, 128, 17) == 0
+    assert A(gdn.GDN_BF16, 128, 128, gdn.CHUNK_SERIAL) == gdn.CHUNK_SERIAL
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=gdn.GDN_BF16, g=FAKE, beta=FAKE, cu=None, cu_host=None, n_seq=1,
+             N=64, H=2, dk=16, dv=16, s0=None, o=FAKE * 64, s1=FAKE * 128, chunk=gdn.CHUNK_SERIAL, ws=None,
+             ws_bytes=0)
+    a.update(kw)
+    L = gdn.lib()
+    st = L.gdn_prefill(a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"], a["cu"], a["cu_host"], a["n_seq"],
+                       a["N"], a["H"], a["dk"], a["dv"], a["s0"], a["o"], a["s1"], a["chunk"], a["ws"],
+                       a["ws_bytes"], None)
+    return st, L.gdn_last_error().decode()
+
+
+def _host(arr):
+    return arr.ctypes.data_as(ctypes.c_void_p).value
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(dtype=5), 3),
+    (dict(H=0), 2),
+    (dict(N=-1), 2),
+    (dict(dk=100, dv=100), 7),
+    (dict(dk=16, dv=32), 7),
+    (dict(chunk=3), 7),
+    (dict(q=None), 1),
+    (dict(beta=None), 1),
+    (dict(s1=None), 1),
+    (dict(q=FAKE + 8), 4),
+    (dict(g=FAKE + 2), 4),
+    (dict(n_seq=2), 5),                      # no cu_seqlens but more than one sequence
+    (dict(o=FAKE), 8),                       # o on top of q
+    (dict(s1=FAKE), 8),                      # final state on top of q
+])
+def test_prefill_validation(kw, code):
+    st, msg = _prefill(**kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_prefill_seqlens_validation():
+    bad = [np.array([0, 10, 5, 64], np.int32), np.array([1, 10, 20, 64], np.int32),
+           np.array([0, 10, 20, 63], np.int32)]
+    for cu in bad:
+        st, msg = _prefill(cu=FAKE * 512, cu_host=_host(cu), n_seq=3)
+        assert st == 5, msg
+    good = np.array([0, 10, 20, 64], np.int32)
+    st, msg = _prefill(cu=FAKE * 512, cu_host=None, n_seq=3)
+    assert st == 1  # device offsets without the host copy
+    st, msg = _prefill(cu=FAKE * 512, cu_host=_host(good), n_seq=3, q=None)
+    assert st == 1
+
+
+def test_decode_validation():
+    L = gdn.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=gdn.GDN_BF16, g=FAKE, beta=FAKE, s=FAKE * 64, o=FAKE * 128, B=4,
+                 H=2, dk=128, dv=128)
+        a.update(kw)
+        return L.gdn_decode_step(a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"], a["s"], a["o"], a["B"],
+                                 a["H"], a["dk"], a["dv"], None)
+
+    assert call(dtype=9) == 3
+    assert call(B=-1) == 2
+    assert call(dk=96, dv=96) == 7
+    assert call(s=None) == 1
+    assert call(o=FAKE + 4) == 4
+    assert call(o=FAKE) == 8
+    assert call(s=FAKE) == 8
+    assert call(B=0) == 0  # nothing to do, nothing enqueued
+
+
+def test_state_calls_validation():
+    L = gdn.lib()
+    assert L.gdn_state_init(None, 2, 4, 128, 128, None, None) == 1
+    assert L.gdn_state_init(FAKE + 4, 2, 4, 128, 128, None, None) == 4
+    assert L.gdn_state_init(FAKE, 2, 4, 128, 64, None, None) == 7
+    assert L.gdn_state_init(FAKE, 2, 4, 128, 128, FAKE + 64, None) == 8
+    assert L.gdn_state_init(FAKE, 0, 4, 128, 128, None, None) == 0
+    assert L.gdn_state_reset(FAKE, 2, 4, 128, 128, FAKE, -1, None) == 2
+    assert L.gdn_state_reset(None, 2, 4, 128, 128, None, 0, None) == 1
+
+
+def test_workspace_sizes():
+    assert gdn.prefill_workspace_bytes(4096, 1, 48, 128, 128, gdn.GDN_FP32, 0) == 0
+    assert gdn.prefill_workspace_bytes(4096, 1, 48, 128, 128, gdn.GDN_BF16, gdn.CHUNK_SERIAL) == 0
