@@ -58,7 +58,7 @@ bool overlap(Range a, Range b) {
 int32_t pick_algorithm(gdn_dtype dtype, int32_t dk, int32_t dv, int32_t chunk) {
     if (dtype != GDN_BF16 && dtype != GDN_FP32) return 0;
     if (!supported_d(dk, dv)) return 0;
-    const bool chunked_built = false && dtype == GDN_BF16 && dk == 128;
+    const bool chunked_built = dtype == GDN_BF16 && dk == 128;
     switch (chunk) {
         case GDN_CHUNK_AUTO: return chunked_built ? GDN_CHUNK_64 : GDN_CHUNK_SERIAL;
         case GDN_CHUNK_SERIAL: return GDN_CHUNK_SERIAL;
