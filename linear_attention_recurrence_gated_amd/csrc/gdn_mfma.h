@@ -39,29 +39,40 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
+// Two fp32 -> one dword of two bf16 (round to nearest even; a in the low half).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// (a, b) -> hi = bf16(a), bf16(b) and lo = bf16(a - hi_a), bf16(b - hi_b), one dword each
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = cvt_pk_bf16(a, b);
+    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xFFFF0000u);
+    lo = cvt_pk_bf16(a - ha, b - hb);
+}
+
 // x[0..7] -> (hi, lo) bf16 fragments
 __device__ __forceinline__ void split8(const float (&x)[8], u32x4_t &hi, u32x4_t &lo) {
-    bf16x8_t h, l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        h[e] = (__bf16)x[e];
-        l[e] = (__bf16)(x[e] - (float)h[e]);
+    for (int i = 0; i < 4; ++i) {
+        uint32_t h, l;
+        split2(x[2 * i], x[2 * i + 1], h, l);
+        hi[i] = h;
+        lo[i] = l;
     }
-    hi = __builtin_bit_cast(u32x4_t, h);
-    lo = __builtin_bit_cast(u32x4_t, l);
 }
 
 // x[0..3] -> (hi, lo) halves of a fragment (8 bytes each)
 __device__ __forceinline__ void split4(f32x4_t x, u32x2_t &hi, u32x2_t &lo) {
-    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-    bf16x4_t h, l;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        h[e] = (__bf16)x[e];
-        l[e] = (__bf16)(x[e] - (float)h[e]);
+    for (int i = 0; i < 2; ++i) {
+        uint32_t h, l;
+        split2(x[2 * i], x[2 * i + 1], h, l);
+        hi[i] = h;
+        lo[i] = l;
     }
-    hi = __builtin_bit_cast(u32x2_t, h);
-    lo = __builtin_bit_cast(u32x2_t, l);
 }
 
 // Two accumulator tiles stacked along k -> split B fragment.
