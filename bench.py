@@ -38,6 +38,10 @@ DEC_B, DEC_STEPS = 64, 256
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * D * 2 + 2 * 4 + D * 4        # q, k, v bf16 + g, beta + o fp32 = 1288
 STATE_BYTES_PER_HEAD = D * D * 4                                  # 64 KiB
 PREFILL_FLOP_PER_TOKEN_HEAD = 3 * (C - 1) * D + 2 * (C + 1) * D + 3 * 2 * D * D   # 139,136 (causal count)
+PREFILL_FLOP_FULL_PER_TOKEN_HEAD = 5 * 2 * C * D + 3 * 2 * D * D                    # 180,224 (dense C x C tiles)
+# split of the causal count between the two kernels
+PREP_FLOP_PER_TOKEN_HEAD = (C - 1) * D + (C + 1) * D + 2 * (C - 1) * D             # K K^T, Q K^T, W, U~ = 32,512
+CHAIN_FLOP_PER_TOKEN_HEAD = PREFILL_FLOP_PER_TOKEN_HEAD - PREP_FLOP_PER_TOKEN_HEAD  # 106,624
 DECODE_BYTES_PER_HEAD_TOKEN = 2 * STATE_BYTES_PER_HEAD + 3 * D * 2 + 2 * 4 + D * 4  # 132,360
 
 
@@ -78,50 +82,69 @@ def run_conditions(torch):
     return cond
 
 
-def bench_prefill(torch, gdn, w, steps, warmup):
+def bench_prefill(torch, gdn, w, steps, warmup, rotate):
+    """Times `steps` prefill steps cycling over `rotate` resident copies of the
+    inputs and outputs (rotate > 1 keeps the 256 MB last-level cache from
+    serving one step's inputs to the next)."""
     inp = w.config2(T=T, H=H, d=D)
     dev = "cuda:0"
-    q = w.to_torch(inp.q, "bf16", dev)
-    k = w.to_torch(inp.k, "bf16", dev)
-    v = w.to_torch(inp.v, "bf16", dev)
-    g = torch.from_numpy(inp.g).to(dev)
-    beta = torch.from_numpy(inp.beta).to(dev)
-    o = torch.empty((T, H, D), dtype=torch.float32, device=dev)
-    state = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    q0 = w.to_torch(inp.q, "bf16", dev)
+    k0 = w.to_torch(inp.k, "bf16", dev)
+    v0 = w.to_torch(inp.v, "bf16", dev)
+    g0 = torch.from_numpy(inp.g).to(dev)
+    b0 = torch.from_numpy(inp.beta).to(dev)
+    sets = []
+    for r in range(rotate):
+        sets.append({"q": q0.clone(), "k": k0.clone(), "v": v0.clone(), "g": g0.clone(), "beta": b0.clone(),
+                     "o": torch.empty((T, H, D), dtype=torch.float32, device=dev),
+                     "state": torch.empty((1, H, D, D), dtype=torch.float32, device=dev)})
+    del q0, k0, v0, g0, b0
     ws = torch.empty(gdn.prefill_workspace_bytes(T, 1, H, D, D, gdn.GDN_BF16, gdn.CHUNK_64), dtype=torch.uint8,
                      device=dev)
 
-    def step():
-        gdn.state_init(state)
-        gdn.prefill(q, k, v, g, beta, initial_state=state, final_state=state, out=o, workspace=ws,
-                    chunk=gdn.CHUNK_64)
+    def call(x):
+        gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], initial_state=x["state"], final_state=x["state"],
+                    out=x["o"], workspace=ws, chunk=gdn.CHUNK_64)
 
-    for _ in range(warmup):
-        step()
+    def step(i):
+        x = sets[i % rotate]
+        gdn.state_init(x["state"])
+        call(x)
+
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    for a, b in ev:
+    for i, (a, b) in enumerate(ev):
         a.record()
-        step()
+        step(i)
         b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    # the prefill call alone (its kernels), for the roofline
-    evp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in evp:
-        a.record()
-        gdn.prefill(q, k, v, g, beta, initial_state=state, final_state=state, out=o, workspace=ws,
-                    chunk=gdn.CHUNK_64)
-        b.record()
+    # the prefill call alone, with events between its kernels (library marks):
+    # [0] before the first kernel, [1] after the per-chunk preparation, [2] after the chain
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for m in marks:
+        for e in m:
+            e.record()  # creates the underlying hipEvent_t
     torch.cuda.synchronize()
-    ms_call = sorted(a.elapsed_time(b) for a, b in evp)
+    for i, m in enumerate(marks):
+        gdn.prefill_set_marks(m)
+        call(sets[i % rotate])
+    torch.cuda.synchronize()
+    ms_call = {"call": sorted(m[0].elapsed_time(m[2]) for m in marks),
+               "k_chunk_prep": sorted(m[0].elapsed_time(m[1]) for m in marks),
+               "k_chunk_chain": sorted(m[1].elapsed_time(m[2]) for m in marks)}
     return ms, ms_call, wall
 
 
-def bench_decode(torch, gdn, w, steps):
+def bench_decode(torch, gdn, w, steps, rotate):
+    """One pass of `steps` decode steps; step t updates state copy t % rotate
+    (rotate > 1 stands for successive layers, each with its own state, so the
+    192 MiB state is not served from the last-level cache)."""
     dec = w.config3(steps=steps, B=DEC_B, H=H, d=D)
     dev = "cuda:0"
     q = w.to_torch(dec.q, "bf16", dev)
@@ -130,15 +153,16 @@ def bench_decode(torch, gdn, w, steps):
     g = torch.from_numpy(dec.g).to(dev)
     beta = torch.from_numpy(dec.beta).to(dev)
     s0 = torch.from_numpy(dec.s_init).to(dev)
-    state = torch.empty_like(s0)
+    states = [torch.empty_like(s0) for _ in range(rotate)]
     o = torch.empty((steps, DEC_B, H, D), dtype=torch.float32, device=dev)
 
     def one_pass(events=None):
-        gdn.state_init(state, s0)
+        for st in states:
+            gdn.state_init(st, s0)
         for t in range(steps):
             if events is not None:
                 events[t][0].record()
-            gdn.decode_step(q[t], k[t], v[t], g[t], beta[t], state, out=o[t])
+            gdn.decode_step(q[t], k[t], v[t], g[t], beta[t], states[t % rotate], out=o[t])
             if events is not None:
                 events[t][1].record()
 
@@ -149,6 +173,30 @@ def bench_decode(torch, gdn, w, steps):
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     return ms
+
+
+def bench_copy(torch, gdn, mib, reps):
+    """Calibration run for the HBM byte counters: gdn_state_init copying a
+    state of about `mib` MiB (k_state_fill reads and writes each byte once)."""
+    n = max(1, int(round(mib * 2 ** 20 / (H * D * D * 4))))
+    src = torch.randn((n, H, D, D), dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        gdn.state_init(dst, src)
+        b.record()
+    torch.cuda.synchronize()
+    if not torch.equal(dst, src):
+        raise RuntimeError("copy calibration: state_init copy mismatch")
+    ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+    nbytes = src.numel() * 4
+    return {"only": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "mean_ms": ms,
+            "gbs": 2 * nbytes / (ms / 1e3) / 1e9}
+
+
+def mean(xs):
+    return sum(xs) / len(xs)
 
 
 def pct(xs, p):
@@ -186,8 +234,14 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=DEC_STEPS)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time one half only and print its numbers (for profiling runs)")
+    ap.add_argument("--only", default=None,
+                    help="comma list of parts to time alone (prefill, decode, copy), one JSON line each, for "
+                         "profiling runs; 'copy' is the byte-counter calibration copy")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time one resident copy (inputs and state may then sit in the last-level cache)")
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="resident copies of the inputs/states cycled through by successive steps")
+    ap.add_argument("--copy-mib", type=float, default=1024.0, help="size of the calibration copy")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the recurrence shards across heads and sequences with no "
@@ -202,27 +256,41 @@ def main():
         sys.exit(2)
     gdn.lib()  # fail loudly if the HIP library is missing
 
-    if args.only == "prefill":
-        ms, ms_call, _ = bench_prefill(torch, gdn, w, args.steps, args.warmup)
-        print(json.dumps({"only": "prefill", "ms_per_step": sum(ms) / len(ms),
-                          "call_mean_ms": sum(ms_call) / len(ms_call)}), flush=True)
+    if args.only:
+        parts = args.only.split(",")
+        bad = [p for p in parts if p not in ("prefill", "decode", "copy")]
+        if bad:
+            ap.error(f"--only: unknown part(s) {bad}")
+        for part in parts:
+            if part == "prefill":
+                ms, ms_call, _ = bench_prefill(torch, gdn, w, args.steps, args.warmup, args.rotate)
+                print(json.dumps({"only": "prefill", "ms_per_step": mean(ms),
+                                  **{k + "_mean_ms": mean(x) for k, x in ms_call.items()}}), flush=True)
+            elif part == "decode":
+                dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
+                print(json.dumps({"only": "decode", "ms_per_step": mean(dec_ms)}), flush=True)
+            else:
+                print(json.dumps(bench_copy(torch, gdn, args.copy_mib, max(1, args.steps))), flush=True)
         return
-    if args.only == "decode":
-        dec_ms = bench_decode(torch, gdn, w, args.decode_steps)
-        print(json.dumps({"only": "decode", "ms_per_step": sum(dec_ms) / len(dec_ms)}), flush=True)
-        return
-    ms, ms_call, wall = bench_prefill(torch, gdn, w, args.steps, args.warmup)
-    dec_ms = bench_decode(torch, gdn, w, args.decode_steps)
+    ms, ms_call, wall = bench_prefill(torch, gdn, w, args.steps, args.warmup, args.rotate)
+    dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
 
-    step_ms = sum(ms) / len(ms)
+    step_ms = mean(ms)
     tok_s = T / (step_ms / 1e3)
-    call_ms = sum(ms_call) / len(ms_call)
+    prep_ms, chain_ms, call_ms = mean(ms_call["k_chunk_prep"]), mean(ms_call["k_chunk_chain"]), mean(ms_call["call"])
     prefill_bytes = PREFILL_BYTES_PER_TOKEN_HEAD * T * H + 2 * STATE_BYTES_PER_HEAD * H
     prefill_flop = PREFILL_FLOP_PER_TOKEN_HEAD * T * H
-    ach_gbs = prefill_bytes / (call_ms / 1e3) / 1e9
+    kern_ms = prep_ms + chain_ms
+    ach_gbs = prefill_bytes / (kern_ms / 1e3) / 1e9
     ach_tflops = prefill_flop / (call_ms / 1e3) / 1e12
+    prep_tflops = PREP_FLOP_PER_TOKEN_HEAD * T * H / (prep_ms / 1e3) / 1e12
+    chain_tflops = CHAIN_FLOP_PER_TOKEN_HEAD * T * H / (chain_ms / 1e3) / 1e12
+    traffic = None
+    tp, tc = load_traffic("k_chunk_prep"), load_traffic("k_chunk_chain")
+    if tp is not None and tc is not None:
+        traffic = tp + tc
 
-    dec_step_ms = sum(dec_ms) / len(dec_ms)
+    dec_step_ms = mean(dec_ms)
     dec_bytes = DECODE_BYTES_PER_HEAD_TOKEN * DEC_B * H
     dec_gbs = dec_bytes / (dec_step_ms / 1e3) / 1e9
 
@@ -241,23 +309,46 @@ def main():
         "data": "synthetic",
         "config": {"workload": "gated delta-rule prefill, 1 sequence x 4096 tokens, 48 heads, d_k=d_v=128, "
                                "bf16 q/k/v, fp32 g/beta/state/o, chunk 64; plus 256 decode steps on 64 "
-                               "sequences x 48 heads",
+                               "sequences x 48 heads; successive steps cycle over `rotate` resident copies",
                    "batch": 1, "seq_len": T, "heads": H, "head_dim": D, "chunk": C,
                    "decode_batch": DEC_B, "decode_steps": args.decode_steps, "state_dtype": "fp32"},
         "prefill": {"p50_ms": pct(ms, 50), "p95_ms": pct(ms, 95), "p99_ms": pct(ms, 99), "mean_ms": step_ms,
                     "call_mean_ms": call_ms, "algorithmic_tflops": ach_tflops,
-                    "mfma_frac": ach_tflops / BF16_MFMA_PEAK_TFLOPS, "wall_s": wall},
-        "roofline": {"kernel": "gdn_prefill (k_chunk_prep + k_chunk_chain)", "bound": "hbm",
+                    "mfma_frac": ach_tflops / BF16_MFMA_PEAK_TFLOPS,
+                    "mfma_frac_full_tiles": PREFILL_FLOP_FULL_PER_TOKEN_HEAD * T * H / (call_ms / 1e3) / 1e12
+                    / BF16_MFMA_PEAK_TFLOPS, "wall_s": wall,
+                    "kernels": {
+                        "k_chunk_prep": {"mean_ms": prep_ms, "p50_ms": pct(ms_call["k_chunk_prep"], 50),
+                                         "algorithmic_tflops": prep_tflops,
+                                         "mfma_frac": prep_tflops / BF16_MFMA_PEAK_TFLOPS,
+                                         "traffic": tp},
+                        "k_chunk_chain": {"mean_ms": chain_ms, "p50_ms": pct(ms_call["k_chunk_chain"], 50),
+                                          "algorithmic_tflops": chain_tflops,
+                                          "mfma_frac": chain_tflops / BF16_MFMA_PEAK_TFLOPS,
+                                          "traffic": tc}}},
+        "roofline": {"kernel": "k_chunk_prep + k_chunk_chain (the two launches of one gdn_prefill call, "
+                               "timed live by library event marks)", "bound": "hbm",
                      "achieved": ach_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach_gbs / HBM_PEAK_GBS,
-                     "traffic": load_traffic("gdn_prefill")},
+                     "traffic": traffic, "algorithmic_bytes": prefill_bytes, "mean_ms": kern_ms},
         "decode": {"value": dec_gbs, "unit": "GB/s", "pct_hbm_peak": 100.0 * dec_gbs / HBM_PEAK_GBS,
                    "ms_per_step": dec_step_ms, "p50_ms": pct(dec_ms, 50), "p95_ms": pct(dec_ms, 95),
                    "p99_ms": pct(dec_ms, 99), "tokens_per_s_layer": DEC_B / (dec_step_ms / 1e3),
                    "roofline": {"kernel": "k_decode_step", "bound": "hbm", "achieved": dec_gbs,
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                                 "traffic": load_traffic("k_decode_step")}},
+        "rotate": args.rotate,
         "conditions": run_conditions(torch),
     }
+    if args.warm:
+        # the same with one resident copy (inputs and state may be served from the last-level cache)
+        ms_warm, ms_call_warm, _ = bench_prefill(torch, gdn, w, args.steps, args.warmup, 1)
+        dec_ms_warm = bench_decode(torch, gdn, w, args.decode_steps, 1)
+        out["warm_single_copy"] = {
+            "prefill_ms_per_step": mean(ms_warm), "prefill_tokens_per_s_layer": T / (mean(ms_warm) / 1e3),
+            "k_chunk_prep_ms": mean(ms_call_warm["k_chunk_prep"]),
+            "k_chunk_chain_ms": mean(ms_call_warm["k_chunk_chain"]),
+            "decode_ms_per_step": mean(dec_ms_warm),
+            "decode_gbs": dec_bytes / (mean(dec_ms_warm) / 1e3) / 1e9}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -134,6 +134,18 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtyp
                            const float *g, const float *beta, float *state, float *o,
                            int64_t B, int32_t H, int32_t dk, int32_t dv, void *stream);
 
+/* Profiling hook.  Arms up to three caller-owned hipEvent_t handles
+ * (events[0..n_events-1]; NULL entries are skipped) for the NEXT gdn_prefill
+ * call made by this host thread, which records them on its stream:
+ *   events[0] before its first kernel,
+ *   events[1] after the state-independent per-chunk kernels (planning and
+ *             chunk preparation; nothing for the token-serial algorithm),
+ *   events[2] after the state chain (its last kernel).
+ * That call disarms the hook whether it succeeds or not; n_events = 0 disarms
+ * it at once.  Returns GDN_ERR_SHAPE for n_events outside [0, 3] and
+ * GDN_ERR_NULL for a NULL array with n_events > 0 (the hook is then disarmed). */
+gdn_status gdn_prefill_set_marks(void *const *events, int32_t n_events);
+
 /* Static description of a status code. */
 const char *gdn_status_string(gdn_status status);
 

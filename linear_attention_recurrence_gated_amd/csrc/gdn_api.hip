@@ -15,6 +15,18 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Events armed by gdn_prefill_set_marks for the next gdn_prefill on this thread.
+struct Marks {
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+};
+thread_local Marks g_marks;
+
+Marks take_marks() {
+    Marks m = g_marks;
+    g_marks = Marks{};
+    return m;
+}
+
 gdn_status fail(gdn_status st, const char *fmt, ...) {
     char buf[512];
     va_list ap;
@@ -108,6 +120,14 @@ const char *gdn_status_string(gdn_status s) {
 
 const char *gdn_last_error(void) { return g_last_error.c_str(); }
 
+gdn_status gdn_prefill_set_marks(void *const *events, int32_t n_events) {
+    g_marks = Marks{};
+    if (n_events < 0 || n_events > 3) return fail(GDN_ERR_SHAPE, "prefill_set_marks: n_events=%d outside [0, 3]", n_events);
+    if (n_events > 0 && !events) return fail(GDN_ERR_NULL, "prefill_set_marks: events is NULL");
+    for (int i = 0; i < n_events; ++i) g_marks.ev[i] = static_cast<hipEvent_t>(events[i]);
+    return ok();
+}
+
 gdn_status gdn_state_init(float *state, int64_t n_seq, int32_t H, int32_t dk, int32_t dv, const float *init,
                           void *stream) {
     if (n_seq < 0 || H <= 0) return fail(GDN_ERR_SHAPE, "state_init: n_seq=%lld H=%d", (long long)n_seq, H);
@@ -155,6 +175,7 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
                        int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, const float *initial_state,
                        float *o, float *final_state, int32_t chunk, void *workspace, size_t workspace_bytes,
                        void *stream) {
+    const Marks marks = take_marks();
     if (dtype != GDN_BF16 && dtype != GDN_FP32) return fail(GDN_ERR_DTYPE, "prefill: dtype %d", (int)dtype);
     if (n_seq < 0 || total_tokens < 0 || H <= 0 || total_tokens > (int64_t)INT32_MAX)
         return fail(GDN_ERR_SHAPE, "prefill: n_seq=%lld total_tokens=%lld H=%d", (long long)n_seq,
@@ -217,11 +238,12 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
         for (Range in : {rq, rk, rv, rg, rb, rs0, rcu, ro, rs1})
             if (overlap({workspace, need}, in)) return fail(GDN_ERR_ALIAS, "prefill: workspace overlaps an argument");
         return hip_status(gdn::launch_prefill_chunked(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, n_seq,
-                                                      total_tokens, H, initial_state, o, final_state, workspace, st),
+                                                      total_tokens, H, initial_state, o, final_state, workspace,
+                                                      marks.ev, st),
                           "prefill (chunked) launch");
     }
     return hip_status(gdn::launch_prefill_serial(dtype == GDN_BF16, dk, q, k, v, g, beta, cu_seqlens, n_seq,
-                                                 total_tokens, H, initial_state, o, final_state, st),
+                                                 total_tokens, H, initial_state, o, final_state, marks.ev, st),
                       "prefill (serial) launch");
 }
 

@@ -616,8 +616,11 @@ size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int 
 hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, const float *g, const float *beta,
                                   const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
                                   int64_t total_tokens, int H, const float *initial_state, float *o,
-                                  float *final_state, void *workspace, hipStream_t stream) {
+                                  float *final_state, void *workspace, const hipEvent_t *marks,
+                                  hipStream_t stream) {
     const WsLayout L = ws_layout(total_tokens, n_seq, H);
+    hipError_t e = record_mark(marks[0], stream);
+    if (e != hipSuccess) return e;
     char *ws = static_cast<char *>(workspace);
     int32_t *chunk_base = cu_seqlens ? reinterpret_cast<int32_t *>(ws + L.base_off) : nullptr;
     int32_t *seq_order = cu_seqlens ? reinterpret_cast<int32_t *>(ws + L.order_off) : nullptr;
@@ -626,7 +629,7 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     if (cu_seqlens) {
         for (int64_t s = 0; s < n_seq; ++s) n_chunks += (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + C - 1) / C;
         hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, stream, cu_seqlens, (int)n_seq, chunk_base, seq_order);
-        hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else {
         n_chunks = (total_tokens + C - 1) / C;
@@ -636,14 +639,19 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
                            static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                            static_cast<const uint16_t *>(v), g, beta, cu_seqlens, chunk_base, (int)n_seq,
                            total_tokens, H, recs);
-        hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    e = record_mark(marks[1], stream);
+    if (e != hipSuccess) return e;
     if (chain_waves(n_seq * H) == 4)
-        return launch_chain<4>(q, k, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
-                               final_state, recs, stream);
-    return launch_chain<2>(q, k, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
-                           final_state, recs, stream);
+        e = launch_chain<4>(q, k, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
+                            final_state, recs, stream);
+    else
+        e = launch_chain<2>(q, k, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
+                            final_state, recs, stream);
+    if (e != hipSuccess) return e;
+    return record_mark(marks[2], stream);
 }
 
 }  // namespace gdn

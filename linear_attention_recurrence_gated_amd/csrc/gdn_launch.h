@@ -14,13 +14,17 @@ hipError_t launch_decode(bool bf16, int d, const void *q, const void *k, const v
                          const float *g, const float *beta, float *state, float *o,
                          int64_t BH, hipStream_t stream);
 
+// marks[3]: events (or nullptr) recorded on `stream` before the first kernel,
+// after the state-independent kernels and after the state chain.
+hipError_t record_mark(hipEvent_t ev, hipStream_t stream);
+
 // Token-serial prefill: one workgroup per (sequence, head, row tile) walks the
 // sequence's tokens in order.
 hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k, const void *v,
                                  const float *g, const float *beta, const int32_t *cu_seqlens,
                                  int64_t n_seq, int64_t total_tokens, int H,
                                  const float *initial_state, float *o, float *final_state,
-                                 hipStream_t stream);
+                                 const hipEvent_t *marks, hipStream_t stream);
 
 // Chunkwise-parallel prefill (64-token chunks, d = 128, bf16 q/k/v).
 size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H);
@@ -29,7 +33,7 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v,
                                   const int32_t *cu_seqlens_host, int64_t n_seq,
                                   int64_t total_tokens, int H, const float *initial_state,
                                   float *o, float *final_state, void *workspace,
-                                  hipStream_t stream);
+                                  const hipEvent_t *marks, hipStream_t stream);
 
 // state[0 : n_floats] = init ? init : 0
 hipError_t launch_state_fill(float *state, const float *init, int64_t n_floats, hipStream_t stream);

@@ -209,22 +209,29 @@ static hipError_t serial_d(const void *q, const void *k, const void *v, const fl
 hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k, const void *v, const float *g,
                                  const float *beta, const int32_t *cu_seqlens, int64_t n_seq,
                                  int64_t total_tokens, int H, const float *initial_state, float *o,
-                                 float *final_state, hipStream_t stream) {
+                                 float *final_state, const hipEvent_t *marks, hipStream_t stream) {
     if (n_seq == 0) return hipSuccess;
+    hipError_t e = record_mark(marks[0], stream);
+    if (e == hipSuccess) e = record_mark(marks[1], stream);
+    if (e != hipSuccess) return e;
 #define GDN_SER(D)                                                                                         \
     case D:                                                                                                \
-        return bf16 ? serial_d<uint16_t, D>(q, k, v, g, beta, cu_seqlens, n_seq, total_tokens, H,         \
-                                            initial_state, o, final_state, stream)                         \
-                    : serial_d<float, D>(q, k, v, g, beta, cu_seqlens, n_seq, total_tokens, H,            \
-                                         initial_state, o, final_state, stream);
+        e = bf16 ? serial_d<uint16_t, D>(q, k, v, g, beta, cu_seqlens, n_seq, total_tokens, H,             \
+                                         initial_state, o, final_state, stream)                            \
+                 : serial_d<float, D>(q, k, v, g, beta, cu_seqlens, n_seq, total_tokens, H,                \
+                                      initial_state, o, final_state, stream);                              \
+        break;
     switch (d) {
         GDN_SER(16)
         GDN_SER(32)
         GDN_SER(64)
         GDN_SER(128)
+        default:
+            return hipErrorInvalidValue;
     }
 #undef GDN_SER
-    return hipErrorInvalidValue;
+    if (e != hipSuccess) return e;
+    return record_mark(marks[2], stream);
 }
 
 }  // namespace gdn

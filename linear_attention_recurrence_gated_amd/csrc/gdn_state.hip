@@ -52,4 +52,8 @@ hipError_t launch_state_reset_slots(float *state, const int32_t *slots, int32_t 
     return hipGetLastError();
 }
 
+hipError_t record_mark(hipEvent_t ev, hipStream_t stream) {
+    return ev ? hipEventRecord(ev, stream) : hipSuccess;
+}
+
 }  // namespace gdn

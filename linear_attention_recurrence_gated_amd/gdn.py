@@ -8,6 +8,7 @@ Names mirror include/gdn.h:
     prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=0) -> (o, final_state)
     decode_step(q, k, v, g, beta, state) -> o          (state updated in place)
     state_init(state, init=None), state_reset(state, slots=None)
+    prefill_set_marks([ev0, ev1, ev2])                 (profiling hook)
     state_bytes(...), prefill_workspace_bytes(...), prefill_algorithm(...)
 """
 import ctypes
@@ -36,6 +37,7 @@ SIGNATURES = {
     "gdn_prefill": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32,
                            _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "gdn_decode_step": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "gdn_prefill_set_marks": (_i32, [ctypes.POINTER(_vp), _i32]),
     "gdn_status_string": (ctypes.c_char_p, [_i32]),
     "gdn_last_error": (ctypes.c_char_p, []),
 }
@@ -178,6 +180,18 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=CHUNK_A
         _dev_ptr(out, "out", torch.float32), _dev_ptr(final_state, "final_state", torch.float32),
         chunk, ws_ptr, ws_len, _stream(dev, stream)))
     return out, final_state
+
+
+def prefill_set_marks(events):
+    """Arm up to three torch.cuda.Event objects for the next prefill() on this
+    thread: recorded before its first kernel, after the per-chunk kernels and
+    after the state chain.  Each event must have been recorded once already
+    (torch creates the underlying hipEvent_t lazily)."""
+    for e in events:
+        if e is not None and not e.cuda_event:
+            e.record()
+    handles = (_vp * max(3, len(events)))(*[e.cuda_event if e is not None else None for e in events])
+    _check(lib().gdn_prefill_set_marks(handles, len(events)))
 
 
 def decode_step(q, k, v, g, beta, state, out=None, stream=None):

@@ -160,3 +160,13 @@ def test_state_calls_validation():
 def test_workspace_sizes():
     assert gdn.prefill_workspace_bytes(4096, 1, 48, 128, 128, gdn.GDN_FP32, 0) == 0
     assert gdn.prefill_workspace_bytes(4096, 1, 48, 128, 128, gdn.GDN_BF16, gdn.CHUNK_SERIAL) == 0
+
+
+def test_prefill_set_marks_validation():
+    L = gdn.lib()
+    arr = (ctypes.c_void_p * 4)()
+    assert L.gdn_prefill_set_marks(arr, 4) == 2
+    assert L.gdn_prefill_set_marks(arr, -1) == 2
+    assert L.gdn_prefill_set_marks(None, 2) == 1
+    assert L.gdn_prefill_set_marks(arr, 3) == 0  # all NULL: armed with nothing
+    assert L.gdn_prefill_set_marks(None, 0) == 0
