@@ -1,7 +1,8 @@
 """Build libgdn.so (gfx950) in-tree from csrc/*.hip with hipcc.
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
-selection switched off, then linked into one shared library next to this file.
+selection switched off and MFMA results kept in ordinary VGPRs, then linked
+into one shared library next to this file.
 """
 import concurrent.futures
 import os
@@ -19,6 +20,9 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: no accumulator-register copies
+    # around the VALU work that reads and rescales MFMA results
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -596,13 +596,13 @@ hipError_t launch_chain(const void *q, const void *k, const int32_t *cu, const i
 
 // Waves per chain workgroup.  Each wave owns 16 rows of S; fewer waves per
 // workgroup means more workgroups (more CUs) per (sequence, head).
-// GDN_CHAIN_WAVES=2|4 overrides the choice (a tuning knob, read once).
+// GDN_CHAIN_WAVES=2|4|8 overrides the choice (a tuning knob, read once).
 int chain_waves(int64_t units) {
     static const int forced = [] {
         const char *e = getenv("GDN_CHAIN_WAVES");
         return e ? atoi(e) : 0;
     }();
-    if (forced == 2 || forced == 4) return forced;
+    if (forced == 2 || forced == 4 || forced == 8) return forced;
     (void)units;
     return 4;  // measured faster than 2 even when 2 would fill more CUs (fewer record copies per head)
 }
@@ -644,7 +644,11 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     }
     e = record_mark(marks[1], stream);
     if (e != hipSuccess) return e;
-    if (chain_waves(n_seq * H) == 4)
+    const int nw = chain_waves(n_seq * H);
+    if (nw == 8)
+        e = launch_chain<8>(q, k, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
+                            final_state, recs, stream);
+    else if (nw == 4)
         e = launch_chain<4>(q, k, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
                             final_state, recs, stream);
     else

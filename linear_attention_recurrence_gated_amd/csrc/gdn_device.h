@@ -67,6 +67,33 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// ---------------------------------------------------------------------------
+// 16-byte state accesses, optionally non-temporal (streamed past the caches:
+// for data touched once per kernel and not again until far more bytes have
+// gone by than the last-level cache holds).
+
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ float4 load_state4(const float *p) {
+    if constexpr (NT) {
+        const f32x4v_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t *>(p));
+        return make_float4(x[0], x[1], x[2], x[3]);
+    } else {
+        return *reinterpret_cast<const float4 *>(p);
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_state4(float *p, float4 y) {
+    if constexpr (NT) {
+        const f32x4v_t x = {y.x, y.y, y.z, y.w};
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4v_t *>(p));
+    } else {
+        *reinterpret_cast<float4 *>(p) = y;
+    }
+}
+
 __device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
 
 __device__ __forceinline__ float4 axpby4(float a, float4 x, float b, float4 y) {

@@ -33,7 +33,8 @@ struct RowLayout {
 
 // ---------------------------------------------------------------------------
 // Decode: grid = B*H workgroups of NW waves; wave w owns rows [w*D/NW, (w+1)*D/NW).
-template <typename TIn, int D, int NW>
+// NT: stream the state with non-temporal loads and stores (large batches).
+template <typename TIn, int D, int NW, bool NT>
 __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                          const TIn *__restrict__ v, const float *__restrict__ g,
                                                          const float *__restrict__ beta, float *__restrict__ state,
@@ -61,8 +62,8 @@ __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__
         const bool ok = rloc < RPW;
         const int row = wave * RPW + (ok ? rloc : 0);
         if (ok) {
-            s0[p] = *reinterpret_cast<const float4 *>(S + row * D + c0);
-            s1[p] = *reinterpret_cast<const float4 *>(S + row * D + c1);
+            s0[p] = load_state4<NT>(S + row * D + c0);
+            s1[p] = load_state4<NT>(S + row * D + c1);
         } else {
             s0[p] = s1[p] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
@@ -78,8 +79,8 @@ __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__
         const float b = group_sum<L::LPR>(dot4(s0[p], q0) + dot4(s1[p], q1));
         const float c = bt * (vr[p] - a);
         if (ok) {
-            *reinterpret_cast<float4 *>(S + row * D + c0) = axpby4(gt, s0[p], c, k0);
-            *reinterpret_cast<float4 *>(S + row * D + c1) = axpby4(gt, s1[p], c, k1);
+            store_state4<NT>(S + row * D + c0, axpby4(gt, s0[p], c, k0));
+            store_state4<NT>(S + row * D + c1, axpby4(gt, s1[p], c, k1));
             if (lr == 0) o[bh * D + row] = gt * b + c * kq;
         }
     }
@@ -169,12 +170,24 @@ __global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q
 
 // ---------------------------------------------------------------------------
 
+// A step's state is read once and written once.  When it is large (here from
+// 32 MiB, an eighth of the MI355X's 256 MB last-level cache), successive steps
+// of a model touch other layers' states in between, so nothing would be reused
+// from that cache: the state then streams with non-temporal accesses, which
+// measured about 15% faster in that regime.  Smaller states keep ordinary
+// accesses and may stay cache-resident from one step to the next.
+constexpr int64_t DECODE_NT_MIN_BYTES = int64_t(32) << 20;
+
 template <typename TIn, int D>
 static hipError_t decode_d(const void *q, const void *k, const void *v, const float *g, const float *beta,
                            float *state, float *o, int64_t BH, hipStream_t stream) {
     constexpr int NW = D >= 64 ? 4 : 1;
-    hipLaunchKernelGGL((k_decode_step<TIn, D, NW>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
-                       (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o);
+    if (BH * D * D * 4 >= DECODE_NT_MIN_BYTES)
+        hipLaunchKernelGGL((k_decode_step<TIn, D, NW, true>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
+                           (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o);
+    else
+        hipLaunchKernelGGL((k_decode_step<TIn, D, NW, false>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
+                           (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o);
     return hipGetLastError();
 }
 
