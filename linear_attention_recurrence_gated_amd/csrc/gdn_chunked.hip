@@ -9,31 +9,34 @@
 //
 //   pseudo-values  u_t = v_t - S_{t-1} k_t  satisfy  (I + L) U = V - diag(e^{G_{t-1}}) K S0^T,
 //                  L[t][s] = beta_s e^{G_{t-1} - G_s} (k_t . k_s)  for s < t
-//   so             U = U~ + W S0^T,   U~ = T V,   W = -T diag(e^{G_{s-1}}) K,   T = (I + L)^{-1}
+//   so             U = T (V - diag(e^{G_{t-1}}) K S0^T),   T = (I + L)^{-1}
 //   outputs        O = diag(e^{G_t}) Q S0^T + P U,   P[t][s] = beta_s e^{G_t - G_s} (q_t . k_s), s <= t
 //   next state     S = e^{G_n} S0 + (diag(beta_t e^{G_n - G_t}) U)^T K
 //
 // Every exponent is a difference G_a - G_b with a >= b, never positive for
-// g <= 1, so nothing overflows however strong the decay.  T, U~, W and P depend
-// only on the chunk's own tokens; only the last three lines touch the state.
-// In a partial chunk the rows past the end are copies of the last row with
-// beta = 0 and lambda = 0; T, W, U~ and P are triangular, so those rows never
-// reach a real row, and beta = 0 keeps them out of the next state.
+// g <= 1, so nothing overflows however strong the decay.  T and P depend only
+// on the chunk's own keys, queries and gates; everything that touches the
+// state is in the last three lines.  In a partial chunk the rows past the end
+// are copies of the last row with beta = 0 and lambda = 0; T and P are lower
+// triangular and beta = 0 zeroes their columns, so those rows never reach a
+// real row, and beta = 0 keeps them out of the next state.
 //
 // Kernels (bf16 q/k/v, d_k = d_v = 128, fp32 gates, state and outputs):
 //   k_plan         varlen only: per-sequence chunk offsets and a longest-first order.
 //   k_chunk_prep   one 4-wave workgroup per (chunk, head), all in parallel:
-//                  K K^T and Q K^T on MFMA, the masked L and P, T = (I + L)^{-1}
-//                  by 16x16 blocks, then W and U~ on MFMA.  It writes one record
-//                  per (chunk, head): W and P as split bf16 MFMA fragments, U~
-//                  in accumulator layout, and the gate factors e^{G_t},
-//                  beta_t e^{G_n - G_t}, e^{G_n}.
+//                  K K^T and Q K^T on MFMA, the masked L and P, and
+//                  T = (I + L)^{-1} by 16x16 blocks.  It writes a 25 KiB record
+//                  per (chunk, head): T and P as split bf16 MFMA fragments and
+//                  the gate factors e^{G_t}, beta_t e^{G_n - G_t}, e^{G_n},
+//                  e^{G_{t-1}}.
 //   k_chunk_chain  one workgroup per (sequence, head, 16*NW rows of S), walking
-//                  the sequence's chunks with S^T in MFMA accumulators.  The
-//                  record, q and k of the next chunk stream into LDS with direct
-//                  global->LDS loads while the current chunk computes (double
-//                  buffer, one barrier per chunk).  Each wave owns 16 rows of S:
-//                  rows are independent, so tiles of one head never exchange data.
+//                  the sequence's chunks with S^T in MFMA accumulators.  NW
+//                  copy waves stream the record and the q, k, v rows of the
+//                  next chunk into LDS with direct global->LDS loads while NW
+//                  compute waves work on the current chunk (double buffer, one
+//                  barrier per chunk).  Each compute wave owns 16 rows of S:
+//                  rows are independent, so the waves and workgroups of one
+//                  head never exchange data.
 //
 // q, k and v chunks live in LDS as row tiles: 64 token rows of 256 bytes whose
 // 16-byte units are XOR-swizzled by (row & 15).  The swizzle is applied by the
@@ -59,18 +62,22 @@ constexpr int DK = 128;  // head dimension (d_k = d_v)
 __host__ __device__ constexpr int tblk(int tb, int ks) { return tb < 2 ? tb : 2 + 2 * (tb - 2) + ks; }
 constexpr int T_BLOCKS = 6;
 
-// One record per (chunk, head) in the workspace.  The first REC_DMA bytes are
-// copied verbatim into LDS by the chain kernel.
+// One record per (chunk, head) in the workspace, copied verbatim into LDS by
+// the chain kernel.  Fragments of a lower-triangular 64x64 matrix are the
+// T_BLOCKS nonzero 16x32 blocks tblk(tb, ks), each split into hi and lo bf16.
 constexpr int FRAG = 1024;                            // 64 lanes x 16 bytes
-constexpr int REC_W_HI = 0;                           // 16 fragments (t tile tb, k step kj over d_k): tb * 4 + kj
-constexpr int REC_W_LO = REC_W_HI + 16 * FRAG;
-constexpr int REC_P_HI = REC_W_LO + 16 * FRAG;        // 6 fragments, tblk(tb, ks)
+constexpr int REC_T_HI = 0;                           // T = (I + L)^{-1}
+constexpr int REC_T_LO = REC_T_HI + T_BLOCKS * FRAG;
+constexpr int REC_P_HI = REC_T_LO + T_BLOCKS * FRAG;  // P
 constexpr int REC_P_LO = REC_P_HI + T_BLOCKS * FRAG;
-constexpr int REC_GATE = REC_P_LO + T_BLOCKS * FRAG;  // e^{G_t}[64], beta_t e^{G_n - G_t}[64], e^{G_n}
-constexpr int REC_DMA = REC_GATE + FRAG;              // 45 KiB
-constexpr int REC_U = REC_DMA;                        // U~ accumulator tiles (tb * 8 + it), 64 lanes x f32x4
-constexpr int REC_BYTES = REC_U + 32 * FRAG;          // 77 KiB
-static_assert(REC_DMA % FRAG == 0 && REC_BYTES % 256 == 0, "record layout");
+constexpr int REC_GATE = REC_P_LO + T_BLOCKS * FRAG;  // floats, below
+constexpr int GATE_EG = 0;                            // e^{G_t}, t = 0..63
+constexpr int GATE_BW = 64;                           // beta_t e^{G_n - G_t}
+constexpr int GATE_EGN = 128;                         // e^{G_n}
+constexpr int GATE_EGM1 = 192;                        // e^{G_{t-1}}
+constexpr int REC_BYTES = REC_GATE + FRAG;            // 25 KiB
+constexpr int REC_PIECES = REC_BYTES / FRAG;
+static_assert(REC_BYTES % 256 == 0, "record layout");
 
 constexpr int TILE = C * DK * 2;  // one bf16 row tile: 16 KiB
 
@@ -215,12 +222,11 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t *__restrict__ cu, in
 // k_chunk_prep: one 4-wave workgroup per (global chunk, head).
 
 struct PrepSmem {
-    __attribute__((aligned(16))) char K[TILE];  // row tiles of the chunk
-    __attribute__((aligned(16))) char V[TILE];
+    __attribute__((aligned(16))) char K[TILE];   // row tiles of the chunk
     __attribute__((aligned(16))) char QT[TILE];  // Q while P is formed, then T (fp32, swizzled 16-byte units)
     float L[64][68];                             // L (strictly lower triangular)
     float Y[3][16][16];                          // per-level block products
-    float G[64], B[64], eGm1[64];
+    float G[64], B[64];
 };
 
 // T[t][s] in the QT region: 16-byte unit (s >> 2) of row t XOR-swizzled by (t & 15).
@@ -232,8 +238,8 @@ __device__ __forceinline__ float4 t4(const char *qt, int t, int s4) {  // T[t][s
 }
 
 __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                                    const uint16_t *__restrict__ v, const float *__restrict__ g,
-                                                    const float *__restrict__ beta, const int32_t *__restrict__ cu,
+                                                    const float *__restrict__ g, const float *__restrict__ beta,
+                                                    const int32_t *__restrict__ cu,
                                                     const int32_t *__restrict__ chunk_base, int n_seq,
                                                     int64_t total_tokens, int H, char *__restrict__ recs) {
     const int64_t gc = blockIdx.x / H;
@@ -249,9 +255,8 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
 
     __shared__ PrepSmem S;
 
-    // q, k, v rows of the chunk -> LDS row tiles (12 one-kilobyte copies per wave)
+    // q, k rows of the chunk -> LDS row tiles (8 one-kilobyte copies per wave)
     dma_rows(S.K, k + cbase, rs, n, lane, wave, 4);
-    dma_rows(S.V, v + cbase, rs, n, lane, wave, 4);
     dma_rows(S.QT, q + cbase, rs, n, lane, wave, 4);
     if (wave == 0) {  // gate prefix sums and the record's gate factors
         const int64_t off = (t0 + min(lane, n - 1)) * H + h;
@@ -263,11 +268,11 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
         const float G63 = __shfl(G, 63, 64);
         S.G[lane] = G;
         S.B[lane] = bt;
-        S.eGm1[lane] = lane > 0 ? __expf(Gm1) : 1.f;
         float *gate = reinterpret_cast<float *>(rec + REC_GATE);
-        gate[lane] = __expf(G);
-        gate[64 + lane] = bt * __expf(G63 - G);
-        if (lane == 63) gate[128] = __expf(G63);
+        gate[GATE_EG + lane] = __expf(G);
+        gate[GATE_BW + lane] = bt * __expf(G63 - G);
+        gate[GATE_EGM1 + lane] = lane > 0 ? __expf(Gm1) : 1.f;
+        if (lane == 63) gate[GATE_EGN] = __expf(G63);
     }
     wait_all_vmem();
     __syncthreads();
@@ -384,53 +389,16 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
         }
     }
 
-    // W fragment pairs and U~ tile pairs: item i -> t tile tb = i >> 3, u = i & 7
-    for (int i = wave; i < 32; i += 4) {
-        const int tb = i >> 3, u = i & 7;
-        const bool is_w = u < 4;
-        u32x4_t fh[2], fl[2];
-        const int nks = (tb >> 1) + 1;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            fh[ks] = fl[ks] = u32x4_t{0u, 0u, 0u, 0u};
-            if (ks < nks) {
-                const float4 a = t4(S.QT, 16 * tb + r, 32 * ks + 4 * g4);
-                const float4 b = t4(S.QT, 16 * tb + r, 32 * ks + 16 + 4 * g4);
-                float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                if (is_w) {  // -T diag(e^{G_{s-1}}) for W
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] *= -S.eGm1[32 * ks + slot_k(g4, e)];
-                }
-                split8(x, fh[ks], fl[ks]);
-            }
-        }
-        if (is_w) {  // W^T tiles (jm, tb) for jm = 2u, 2u + 1 -> W fragment (tb, kj = u)
-            u32x2_t hi[2], lo[2];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int jm = 2 * u + half;
-                f32x4_t acc = zero4();
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks < nks) acc = mfma2b(colfrag(S.K, ks, jm, g4, lane), fh[ks], fl[ks], acc);
-                split4(acc, hi[half], lo[half]);
-            }
-            const int blk = tb * 4 + u;
-            *reinterpret_cast<u32x4_t *>(rec + REC_W_HI + blk * FRAG + lane * 16) =
-                u32x4_t{hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
-            *reinterpret_cast<u32x4_t *>(rec + REC_W_LO + blk * FRAG + lane * 16) =
-                u32x4_t{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
-        } else {  // U~ = T V tiles (tb, it) for it = 2(u - 4), 2(u - 4) + 1
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int it = 2 * (u - 4) + half;
-                f32x4_t acc = zero4();
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks < nks) acc = mfma2a(fh[ks], fl[ks], colfrag(S.V, ks, it, g4, lane), acc);
-                *reinterpret_cast<f32x4_t *>(rec + REC_U + (tb * 8 + it) * FRAG + lane * 16) = acc;
-            }
-        }
+    // T fragments: block tblk(tb, ks), lane (g, r) holds T[16 tb + r][32 ks + slot_k(g, e)], split hi/lo
+    for (int pb = wave; pb < T_BLOCKS; pb += 4) {
+        const int tb = pb < 2 ? pb : 2 + ((pb - 2) >> 1), ks = pb < 2 ? 0 : ((pb - 2) & 1);
+        const float4 a = t4(S.QT, 16 * tb + r, 32 * ks + 4 * g4);
+        const float4 b = t4(S.QT, 16 * tb + r, 32 * ks + 16 + 4 * g4);
+        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        u32x4_t hi, lo;
+        split8(x, hi, lo);
+        *reinterpret_cast<u32x4_t *>(rec + REC_T_HI + pb * FRAG + lane * 16) = hi;
+        *reinterpret_cast<u32x4_t *>(rec + REC_T_LO + pb * FRAG + lane * 16) = lo;
     }
 }
 
@@ -438,16 +406,49 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
 // k_chunk_chain
 
 struct ChainBuf {
-    char rec[REC_DMA];  // head of the chunk record: W, P fragments and gate factors
-    char Q[TILE];       // q rows of the chunk (row tile)
-    char K[TILE];       // k rows of the chunk (row tile)
+    char rec[REC_BYTES];  // the chunk record: T, P fragments and gate factors
+    char Q[TILE];         // q, k, v rows of the chunk (row tiles)
+    char K[TILE];
+    char V[TILE];
 };
+constexpr int CHAIN_PIECES = REC_PIECES + 3 * 16;  // one-kilobyte copies per chunk
 
+// Copy one kilobyte (piece a of 16) of a chunk's token rows into a row tile.
+__device__ __forceinline__ void dma_row_piece(char *tile, const uint16_t *chunk, int rs, int n, int lane, int a) {
+    const int t = 4 * a + (lane >> 4);
+    const int u = (lane & 15) ^ (t & 15);
+    const uint16_t *src = chunk + (uint32_t)(min(t, n - 1) * rs + 8 * u);
+    __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)(tile + a * FRAG), 16, 0, 0);
+}
+
+// Pieces [p0, p1) of one chunk's copies, wave w taking the pieces p = w mod nw:
+// piece p < REC_PIECES is a record kilobyte, the rest are the q, k, v row tiles.
+// Every argument except lane is wave-uniform, so the loop stays scalar.
+__device__ __forceinline__ void chain_copies(ChainBuf &B, const char *rec, const uint16_t *qc, const uint16_t *kc,
+                                             const uint16_t *vc, int rs, int n, int lane, int wave, int nw, int p0,
+                                             int p1) {
+    for (int p = p0 + (wave - p0 % nw + nw) % nw; p < p1; p += nw) {
+        if (p < REC_PIECES) {
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + p * FRAG + lane * 16),
+                                             (lds_void *)(B.rec + p * FRAG), 16, 0, 0);
+        } else {
+            const int x = p - REC_PIECES, which = x >> 4, a = x & 15;
+            if (which == 0) dma_row_piece(B.Q, qc, rs, n, lane, a);
+            else if (which == 1) dma_row_piece(B.K, kc, rs, n, lane, a);
+            else dma_row_piece(B.V, vc, rs, n, lane, a);
+        }
+    }
+}
+
+// NW compute waves (16 rows of S each) and NW copy waves per workgroup.  The
+// copy waves move chunk c + 1 into LDS while the compute waves work on chunk
+// c; one barrier per chunk hands the buffers over.
 template <int NW>
-__global__ __launch_bounds__(64 * NW) void k_chunk_chain(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ seq_order, int n_seq, int64_t total_tokens,
-    int H, const float *initial_state, float *__restrict__ o, float *final_state, const char *__restrict__ recs) {
+__global__ __launch_bounds__(128 * NW) void k_chunk_chain(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ seq_order,
+    int n_seq, int64_t total_tokens, int H, const float *initial_state, float *__restrict__ o, float *final_state,
+    const char *__restrict__ recs) {
     constexpr int TILES = DK / (16 * NW);
     const int bid = blockIdx.x;
     // All row tiles of one (sequence, head) share bid % 8, so they run on one XCD and share its L2.
@@ -462,12 +463,31 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_chain(
     const int64_t cb = cu ? chunk_base[s] : 0;
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
-    const int iw = tile * 16 * NW + 16 * wave;  // first row of S (d_v index) owned by this wave
-    const int it = iw >> 4;
-    const int64_t rs = (int64_t)H * DK;         // elements between consecutive tokens of q, k and o
+    const int rs = H * DK;  // elements between consecutive tokens of q, k, v and o
 
     __shared__ __attribute__((aligned(16))) ChainBuf buf[2];
 
+    if (wave >= NW) {  // copy wave
+        const int cw = wave - NW;
+        for (int c = 0; c <= nc; ++c) {
+            // Iteration c fills the buffer of chunk c; the barrier after it
+            // releases chunk c to the compute waves (the last one only pairs
+            // with their final barrier).
+            if (c < nc) {
+                const int64_t t0 = seq_t0 + (int64_t)c * C;
+                const int n = (int)min((int64_t)C, L - (int64_t)c * C);
+                const int64_t rowbase = (t0 * H + h) * DK;
+                chain_copies(buf[c & 1], recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q + rowbase,
+                             k + rowbase, v + rowbase, rs, n, lane, cw, NW, 0, CHAIN_PIECES);
+                wait_all_vmem();
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    const int iw = tile * 16 * NW + 16 * wave;  // first row of S (d_v index) owned by this wave
+    const int it = iw >> 4;
     // S^T in accumulators: St[jm] lane (g4, r) holds S[iw + r][16 jm + 4 g4 + e]
     f32x4_t St[8];
     const int64_t sbase = ((int64_t)s * H + h) * DK * DK + (int64_t)(iw + r) * DK;
@@ -475,104 +495,97 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_chain(
     for (int jm = 0; jm < 8; ++jm)
         St[jm] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + 16 * jm + 4 * g4) : zero4();
 
-    f32x4_t un[4];  // U~ of the next chunk, straight into registers
-    // Copies for chunk c: q/k rows and U~ right after the barrier, then the
-    // record head in four parts, one before each t tile of the first MFMA phase.
-    auto issue_rows = [&](int c) {
-        const int64_t t0 = seq_t0 + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, L - (int64_t)c * C);
-        const char *rec = recs + ((cb + c) * H + h) * (int64_t)REC_BYTES;
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-            un[tb] = *reinterpret_cast<const f32x4_t *>(rec + REC_U + (tb * 8 + it) * FRAG + lane * 16);
-        ChainBuf &B = buf[c & 1];
-        dma_rows(B.Q, q + (t0 * H + h) * DK, rs, n, lane, wave, NW);
-        dma_rows(B.K, k + (t0 * H + h) * DK, rs, n, lane, wave, NW);
-    };
-    constexpr int REC_PIECES = REC_DMA / FRAG;  // 45
-    auto issue_rec = [&](int c, int part) {     // part 0..3 of the record head
-        const char *rec = recs + ((cb + c) * H + h) * (int64_t)REC_BYTES;
-        ChainBuf &B = buf[c & 1];
-        const int p0 = part * REC_PIECES / 4, p1 = (part + 1) * REC_PIECES / 4;
-        for (int p = p0 + wave; p < p1; p += NW)
-            __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + p * FRAG + lane * 16),
-                                             (lds_void *)(B.rec + p * FRAG), 16, 0, 0);
-    };
-
-    if (nc > 0) {
-        issue_rows(0);
-        for (int part = 0; part < 4; ++part) issue_rec(0, part);
-    }
+    __syncthreads();  // chunk 0 is in buf[0]
     for (int c = 0; c < nc; ++c) {
         const int64_t t0 = seq_t0 + (int64_t)c * C;
         const int n = (int)min((int64_t)C, L - (int64_t)c * C);
-        const bool more = c + 1 < nc;
-        wait_all_vmem();  // this wave's copies for chunk c have landed
-        __syncthreads();  // ... every wave's; and chunk c-1 is finished everywhere, so buf[(c+1)&1] is free
-        f32x4_t Ua[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) Ua[tb] = un[tb];
-        if (more) issue_rows(c + 1);
-
         const ChainBuf &B = buf[c & 1];
-        const u32x4_t *Wh = reinterpret_cast<const u32x4_t *>(B.rec + REC_W_HI);
-        const u32x4_t *Wl = reinterpret_cast<const u32x4_t *>(B.rec + REC_W_LO);
+        const u32x4_t *Th = reinterpret_cast<const u32x4_t *>(B.rec + REC_T_HI);
+        const u32x4_t *Tl = reinterpret_cast<const u32x4_t *>(B.rec + REC_T_LO);
         const u32x4_t *Ph = reinterpret_cast<const u32x4_t *>(B.rec + REC_P_HI);
         const u32x4_t *Pl = reinterpret_cast<const u32x4_t *>(B.rec + REC_P_LO);
         const float *gate = reinterpret_cast<const float *>(B.rec + REC_GATE);
 
-        // U = U~ + W S0^T,  O = diag(e^G) Q S0^T + P U
+        // X = K S0^T and O = Q S0^T (one shared split operand S0^T)
         u32x4_t bSh[4], bSl[4];
 #pragma unroll
         for (int kj = 0; kj < 4; ++kj) split_pair(St[2 * kj], St[2 * kj + 1], bSh[kj], bSl[kj]);
-        f32x4_t O[4];
+        f32x4_t X[4], O[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            if (more) issue_rec(c + 1, tb);
+            X[tb] = zero4();
             O[tb] = zero4();
 #pragma unroll
             for (int kj = 0; kj < 4; ++kj) {
-                Ua[tb] = mfma3(Wh[(tb * 4 + kj) * 64 + lane], Wl[(tb * 4 + kj) * 64 + lane], bSh[kj], bSl[kj], Ua[tb]);
+                X[tb] = mfma2b(rowfrag_slots(B.K, 16 * tb, kj, g4, r), bSh[kj], bSl[kj], X[tb]);
                 O[tb] = mfma2b(rowfrag_slots(B.Q, 16 * tb, kj, g4, r), bSh[kj], bSl[kj], O[tb]);
             }
-            const f32x4_t eg = *reinterpret_cast<const f32x4_t *>(gate + 16 * tb + 4 * g4);
-            O[tb] *= eg;
         }
-        u32x4_t bUh[2], bUl[2];
+        // Y = V - diag(e^{G_{t-1}}) X, in accumulator layout (tiles 2 ks and 2 ks + 1 from one V^T fragment)
+        u32x4_t bYh[2], bYl[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) split_pair(Ua[2 * ks], Ua[2 * ks + 1], bUh[ks], bUl[ks]);
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x4_t vf = colfrag(B.V, ks, it, g4, lane);
+            f32x4_t y[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int tb = 2 * ks + hf;
+                const f32x4_t em = *reinterpret_cast<const f32x4_t *>(gate + GATE_EGM1 + 16 * tb + 4 * g4);
+                const uint32_t w0 = vf[2 * hf], w1 = vf[2 * hf + 1];
+                const f32x4_t vv = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u),
+                                    __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xFFFF0000u)};
+                y[hf] = vv - em * X[tb];
+            }
+            split_pair(y[0], y[1], bYh[ks], bYl[ks]);
+        }
+        // U = T Y
+        f32x4_t U[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
+            U[tb] = zero4();
+#pragma unroll
+            for (int ks = 0; ks <= (tb >> 1); ++ks)
+                U[tb] = mfma3(Th[tblk(tb, ks) * 64 + lane], Tl[tblk(tb, ks) * 64 + lane], bYh[ks], bYl[ks], U[tb]);
+        }
+        // O = diag(e^{G_t}) Q S0^T + P U
+        u32x4_t bUh[2], bUl[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            O[tb] *= *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * tb + 4 * g4);
 #pragma unroll
             for (int ks = 0; ks <= (tb >> 1); ++ks)
                 O[tb] = mfma3(Ph[tblk(tb, ks) * 64 + lane], Pl[tblk(tb, ks) * 64 + lane], bUh[ks], bUl[ks], O[tb]);
         }
-        const int64_t ooff = (int64_t)(4 * g4) * rs + iw + r;
+        float *ob = o + t0 * rs + h * DK;
+        const int ooff = 4 * g4 * rs + iw + r;
         if (n == C) {
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) (o + (t0 + 16 * tb + e) * rs + h * DK)[ooff] = O[tb][e];
+                for (int e = 0; e < 4; ++e) ob[ooff + (16 * tb + e) * rs] = O[tb][e];
         } else {
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (16 * tb + 4 * g4 + e < n) (o + (t0 + 16 * tb + e) * rs + h * DK)[ooff] = O[tb][e];
+                    if (16 * tb + 4 * g4 + e < n) ob[ooff + (16 * tb + e) * rs] = O[tb][e];
         }
 
         // S0^T <- e^{G_n} S0^T + K^T diag(beta_t e^{G_n - G_t}) U
 #pragma unroll
-        for (int a = 0; a < 4; ++a) Ua[a] *= *reinterpret_cast<const f32x4_t *>(gate + 64 + 16 * a + 4 * g4);
+        for (int tb = 0; tb < 4; ++tb) U[tb] *= *reinterpret_cast<const f32x4_t *>(gate + GATE_BW + 16 * tb + 4 * g4);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) split_pair(Ua[2 * ks], Ua[2 * ks + 1], bUh[ks], bUl[ks]);
-        const float eGn = gate[128];
+        for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
+        const float eGn = gate[GATE_EGN];
 #pragma unroll
         for (int jm = 0; jm < 8; ++jm) {
             St[jm] *= eGn;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) St[jm] = mfma2b(colfrag(B.K, ks, jm, g4, lane), bUh[ks], bUl[ks], St[jm]);
         }
+        __syncthreads();  // chunk c + 1 is in the other buffer, and this one is free
     }
 
     float *dst = final_state + sbase;
@@ -581,28 +594,30 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_chain(
 }
 
 template <int NW>
-hipError_t launch_chain(const void *q, const void *k, const int32_t *cu, const int32_t *chunk_base,
+hipError_t launch_chain(const void *q, const void *k, const void *v, const int32_t *cu, const int32_t *chunk_base,
                         const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H,
                         const float *initial_state, float *o, float *final_state, const char *recs,
                         hipStream_t stream) {
     constexpr int TILES = DK / (16 * NW);
     const int64_t units = n_seq * H;
     const int64_t grid = ((units + 7) / 8) * 8 * TILES;
-    hipLaunchKernelGGL((k_chunk_chain<NW>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
-                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), cu, chunk_base, seq_order,
+    hipLaunchKernelGGL((k_chunk_chain<NW>), dim3((unsigned)grid), dim3(128 * NW), 0, stream,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                       static_cast<const uint16_t *>(v), cu, chunk_base, seq_order,
                        (int)n_seq, total_tokens, H, initial_state, o, final_state, recs);
     return hipGetLastError();
 }
 
-// Waves per chain workgroup.  Each wave owns 16 rows of S; fewer waves per
-// workgroup means more workgroups (more CUs) per (sequence, head).
-// GDN_CHAIN_WAVES=2|4|8 overrides the choice (a tuning knob, read once).
+// Compute waves per chain workgroup (it has as many copy waves).  Each compute
+// wave owns 16 rows of S; fewer per workgroup means more workgroups (more
+// CUs) per (sequence, head), each copying the whole chunk.
+// GDN_CHAIN_WAVES=2|4 overrides the choice (a tuning knob, read once).
 int chain_waves(int64_t units) {
     static const int forced = [] {
         const char *e = getenv("GDN_CHAIN_WAVES");
         return e ? atoi(e) : 0;
     }();
-    if (forced == 2 || forced == 4 || forced == 8) return forced;
+    if (forced == 2 || forced == 4) return forced;
     (void)units;
     return 4;  // measured faster than 2 even when 2 would fill more CUs (fewer record copies per head)
 }
@@ -636,23 +651,19 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     }
     if (n_chunks > 0) {
         hipLaunchKernelGGL(k_chunk_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream,
-                           static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                           static_cast<const uint16_t *>(v), g, beta, cu_seqlens, chunk_base, (int)n_seq,
+                           static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), g, beta, cu_seqlens,
+                           chunk_base, (int)n_seq,
                            total_tokens, H, recs);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     e = record_mark(marks[1], stream);
     if (e != hipSuccess) return e;
-    const int nw = chain_waves(n_seq * H);
-    if (nw == 8)
-        e = launch_chain<8>(q, k, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
-                            final_state, recs, stream);
-    else if (nw == 4)
-        e = launch_chain<4>(q, k, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
+    if (chain_waves(n_seq * H) == 4)
+        e = launch_chain<4>(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
                             final_state, recs, stream);
     else
-        e = launch_chain<2>(q, k, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
+        e = launch_chain<2>(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
                             final_state, recs, stream);
     if (e != hipSuccess) return e;
     return record_mark(marks[2], stream);
