@@ -593,6 +593,308 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
     for (int jm = 0; jm < 8; ++jm) *reinterpret_cast<f32x4_t *>(dst + 16 * jm + 4 * g4) = St[jm];
 }
 
+// ---------------------------------------------------------------------------
+// k_chunk_chain_cs: the column-split chain for few (sequence, head) pairs.
+//
+// Four workgroups per (sequence, head), each owning 32 rows of S (two 16-row
+// slices).  Each slice's 128 columns are split over two compute waves of 64
+// columns: a wave forms the partial products K S0^T and Q S0^T over its
+// columns, the pair swaps partials through LDS, and both then hold the full
+// X and Q S0^T of their slice.  Both solve U = T Y (the same 18 MFMAs), each
+// writes two of the four 16-token output tiles, and each updates its own 64
+// columns of S.  Four copy waves stream the next chunk: the record, q and k
+// row tiles, and the workgroup's 32 columns of v (64-byte rows).
+
+constexpr int CS_TILES = 4;             // workgroups per (sequence, head)
+constexpr int VC_BYTES = C * 64;        // 32 columns of v for 64 tokens
+
+struct ChainBufCS {
+    char rec[REC_BYTES];
+    char Q[TILE];
+    char K[TILE];
+    char V[VC_BYTES];
+};
+struct ChainSmemCS {
+    ChainBufCS buf[2];
+    f32x4_t xch[4][8][64];  // per compute wave: partial X (tiles 0..3) and Q S0^T (tiles 4..7), by lane
+    char scratch[FRAG];     // target of the copy waves' padding loads and line touches
+};
+
+// Compact v tile: row t holds 32 columns (64 bytes) at t * 64.  Piece a
+// (one kilobyte) is rows 16a .. 16a + 15; lane l copies row 16a + (l >> 2),
+// columns 8 (l & 3) .. + 7 of the workgroup's 32.
+__device__ __forceinline__ void dma_vcols(char *tile, const uint16_t *chunk, int rs, int n, int lane, int a) {
+    const int t = 16 * a + (lane >> 2);
+    const uint16_t *src = chunk + (uint32_t)(min(t, n - 1) * rs + 8 * (lane & 3));
+    __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)(tile + a * FRAG), 16, 0, 0);
+}
+
+// Fragment of v columns col0 .. col0 + 15 of the compact tile in accumulator
+// order: lane (g, r) gets v[32 ks + slot_k(g, e)][col0 + r], e = 0..7.
+__device__ __forceinline__ u32x4_t vfrag(const char *tile, int ks, int col0, int g4, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int L = lane & 15, e = L >> 2, m = L & 3;
+    const int t0 = 32 * ks + 4 * g4 + e, t1 = t0 + 16;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(tile + t0 * 64 + col0 * 2 + m * 8));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(tile + t1 * 64 + col0 * 2 + m * 8));
+    const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
+    return u32x4_t{a2[0], a2[1], b2[0], b2[1]};
+}
+
+// Copies of one chunk, 16 global->LDS loads per copy wave (the vmcnt waits
+// below rely on that count being the same for every wave): wave 0 copies
+// record kilobytes 0..15, wave 1 record kilobytes 16..24, the four of the v
+// columns and three padding loads (record kilobyte 0 into a scratch
+// kilobyte), wave 2 the q rows and wave 3 the k rows.  Every wave therefore
+// has exactly 16 loads in flight after its copies.
+static_assert(REC_PIECES == 25 && VC_BYTES / FRAG == 4, "copy assignment");
+__device__ __forceinline__ void cs_copies(ChainBufCS &B, char *scratch, const char *rec, const uint16_t *qc,
+                                          const uint16_t *kc, const uint16_t *vc, int rs, int n, int lane, int cw) {
+    if (cw == 0) {
+#pragma unroll
+        for (int a = 0; a < 16; ++a)
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + a * FRAG + lane * 16),
+                                             (lds_void *)(B.rec + a * FRAG), 16, 0, 0);
+    } else if (cw == 1) {
+#pragma unroll
+        for (int a = 16; a < REC_PIECES; ++a)
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + a * FRAG + lane * 16),
+                                             (lds_void *)(B.rec + a * FRAG), 16, 0, 0);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) dma_vcols(B.V, vc, rs, n, lane, a);
+#pragma unroll
+        for (int a = 0; a < 16 - (REC_PIECES - 16) - 4; ++a)
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + lane * 16), (lds_void *)scratch, 16, 0,
+                                             0);
+    } else {
+        const uint16_t *src = cw == 2 ? qc : kc;
+        char *dst = cw == 2 ? B.Q : B.K;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) dma_row_piece(dst, src, rs, n, lane, a);
+    }
+}
+
+// The 128-byte lines of one chunk's copies: the record, then two lines per
+// q, k and v row (rows past n clamped to n - 1).
+constexpr int PF_LINES = REC_BYTES / 128 + 3 * 2 * C;
+#ifndef GDN_PF_DIST
+#define GDN_PF_DIST 3
+#endif
+constexpr int PF_DIST = GDN_PF_DIST;  // chunks between the touch of a chunk's lines and its copies
+
+__device__ __forceinline__ const uint32_t *chunk_line(const char *rec, const uint16_t *q, const uint16_t *k,
+                                                      const uint16_t *v, int64_t rowbase, int rs, int n, int line) {
+    if (line < REC_BYTES / 128) return reinterpret_cast<const uint32_t *>(rec + line * 128);
+    const int x = line - REC_BYTES / 128, which = x / (2 * C), row = (x % (2 * C)) >> 1, half = x & 1;
+    const uint16_t *base = which == 0 ? q : which == 1 ? k : v;
+    return reinterpret_cast<const uint32_t *>(base + rowbase + (uint32_t)(min(row, n - 1) * rs + half * 64));
+}
+
+__global__ __launch_bounds__(512) void k_chunk_chain_cs(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ seq_order,
+    int n_seq, int64_t total_tokens, int H, const float *initial_state, float *__restrict__ o, float *final_state,
+    const char *__restrict__ recs) {
+    const int bid = blockIdx.x;
+    // All workgroups of one (sequence, head) share bid % 8, so they run on one XCD and share its L2.
+    const int u = (bid / (8 * CS_TILES)) * 8 + (bid & 7);
+    const int tile = (bid >> 3) % CS_TILES;
+    if (u >= n_seq * H) return;
+    const int rank = u / H, h = u % H;
+    const int s = seq_order ? seq_order[rank] : rank;
+    const int64_t seq_t0 = cu ? cu[s] : 0;
+    const int64_t L = cu ? (int64_t)cu[s + 1] - seq_t0 : total_tokens;
+    const int nc = (int)((L + C - 1) / C);
+    const int64_t cb = cu ? chunk_base[s] : 0;
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
+    const int rs = H * DK;
+    const int vcol0 = tile * 32;  // the workgroup's first row of S = first column of v
+
+    __shared__ __attribute__((aligned(16))) ChainSmemCS sm;
+
+    if (wave >= 4) {  // copy wave
+        const int cw = wave - 4;
+        auto copies = [=](int c) {
+            const int64_t t0 = seq_t0 + (int64_t)c * C;
+            const int n = (int)min((int64_t)C, L - (int64_t)c * C);
+            const int64_t rowbase = (t0 * H + h) * DK;
+            cs_copies(sm.buf[c & 1], sm.scratch, recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q + rowbase,
+                      k + rowbase, v + rowbase + vcol0, rs, n, lane, cw);
+        };
+        // Touch chunk c: the first 16 bytes of each 128-byte line in this
+        // workgroup's quarter of the lines (the four workgroups of a pair share
+        // them out), copied to a scratch kilobyte of LDS.  The copies of that
+        // chunk, two chunks later, then hit in L2.  Lanes past the quarter
+        // re-touch line 0, so every wave issues exactly one load.
+        auto touch = [=](int c) {
+            int line = tile + CS_TILES * (cw * 64 + lane);
+            if (line >= PF_LINES) line = 0;
+            const int64_t t0 = seq_t0 + (int64_t)c * C;
+            const int n = (int)min((int64_t)C, L - (int64_t)c * C);
+            const uint32_t *src = chunk_line(recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q, k, v,
+                                             (t0 * H + h) * DK, rs, n, line);
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)sm.scratch, 16, 0, 0);
+        };
+        // Barriers: A_0, then per chunk c: X_c, A_{c+1}.  Chunk c + 1 is
+        // copied between X_c and A_{c+1} (its buffer, last used for chunk
+        // c - 1, is free since A_c), so issuing the copies never holds up the
+        // compute waves' exchange at X_c.  These waves make no other LDS
+        // accesses, and their copies are complete once vmcnt says so, so their
+        // barriers are bare (no wait for the touch in flight).
+        if (nc > 0) copies(0);
+        for (int c = 1; c < PF_DIST && c < nc; ++c) touch(c);
+        wait_all_vmem();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // A_0
+        for (int c = 0; c < nc; ++c) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();  // X_c
+            asm volatile("" ::: "memory");
+            if (c + 1 < nc) copies(c + 1);
+            if (c + PF_DIST < nc) {
+                touch(c + PF_DIST);  // issued after every copy of this iteration
+                __builtin_amdgcn_s_waitcnt(0x0F71);  // vmcnt(1): everything but the newest touch has landed
+            } else {
+                wait_all_vmem();
+            }
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();  // A_{c+1}
+        }
+        return;
+    }
+
+    const int sl = wave >> 1, hf = wave & 1;  // row slice, column half
+    const int iw = tile * 32 + 16 * sl;       // first row of S owned by this wave
+    // S^T in accumulators, this wave's 64 columns: St[j] lane (g4, r) holds S[iw + r][16 (4 hf + j) + 4 g4 + e]
+    f32x4_t St[4];
+    const int64_t sbase = ((int64_t)s * H + h) * DK * DK + (int64_t)(iw + r) * DK + 64 * hf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        St[j] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + 16 * j + 4 * g4) : zero4();
+    // output tiles of this wave: {0, 3} or {1, 2} (balanced P U work)
+    const int ta = hf ? 1 : 0, tz = hf ? 2 : 3;
+
+    __syncthreads();  // A_0: chunk 0 is in buf[0]
+    for (int c = 0; c < nc; ++c) {
+        const int64_t t0 = seq_t0 + (int64_t)c * C;
+        const int n = (int)min((int64_t)C, L - (int64_t)c * C);
+        const ChainBufCS &B = sm.buf[c & 1];
+        const u32x4_t *Th = reinterpret_cast<const u32x4_t *>(B.rec + REC_T_HI);
+        const u32x4_t *Tl = reinterpret_cast<const u32x4_t *>(B.rec + REC_T_LO);
+        const u32x4_t *Ph = reinterpret_cast<const u32x4_t *>(B.rec + REC_P_HI);
+        const u32x4_t *Pl = reinterpret_cast<const u32x4_t *>(B.rec + REC_P_LO);
+        const float *gate = reinterpret_cast<const float *>(B.rec + REC_GATE);
+
+        // partial X = K S0^T and Q S0^T over this wave's 64 columns (k steps 2 hf, 2 hf + 1)
+        u32x4_t bSh[2], bSl[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) split_pair(St[2 * kk], St[2 * kk + 1], bSh[kk], bSl[kk]);
+        f32x4_t X[4], O[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            X[tb] = zero4();
+            O[tb] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                X[tb] = mfma2b(rowfrag_slots(B.K, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], X[tb]);
+                O[tb] = mfma2b(rowfrag_slots(B.Q, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], O[tb]);
+            }
+            sm.xch[wave][tb][lane] = X[tb];
+            sm.xch[wave][4 + tb][lane] = O[tb];
+        }
+        __syncthreads();  // X_c: partials visible
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) X[tb] += sm.xch[wave ^ 1][tb][lane];
+        O[ta] += sm.xch[wave ^ 1][4 + ta][lane];
+        O[tz] += sm.xch[wave ^ 1][4 + tz][lane];
+
+        // Y = V - diag(e^{G_{t-1}}) X
+        u32x4_t bYh[2], bYl[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x4_t vf = vfrag(B.V, ks, 16 * sl, g4, lane);
+            f32x4_t y[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int tb = 2 * ks + hh;
+                const f32x4_t em = *reinterpret_cast<const f32x4_t *>(gate + GATE_EGM1 + 16 * tb + 4 * g4);
+                const uint32_t w0 = vf[2 * hh], w1 = vf[2 * hh + 1];
+                const f32x4_t vv = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u),
+                                    __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xFFFF0000u)};
+                y[hh] = vv - em * X[tb];
+            }
+            split_pair(y[0], y[1], bYh[ks], bYl[ks]);
+        }
+        // U = T Y
+        f32x4_t U[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            U[tb] = zero4();
+#pragma unroll
+            for (int ks = 0; ks <= (tb >> 1); ++ks)
+                U[tb] = mfma3(Th[tblk(tb, ks) * 64 + lane], Tl[tblk(tb, ks) * 64 + lane], bYh[ks], bYl[ks], U[tb]);
+        }
+        // O = diag(e^{G_t}) Q S0^T + P U for this wave's two tiles
+        u32x4_t bUh[2], bUl[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
+        float *ob = o + t0 * rs + h * DK;
+        const int ooff = 4 * g4 * rs + iw + r;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tb = i ? tz : ta;
+            f32x4_t acc = O[tb] * *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * tb + 4 * g4);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                if (ks <= (tb >> 1))
+                    acc = mfma3(Ph[tblk(tb, ks) * 64 + lane], Pl[tblk(tb, ks) * 64 + lane], bUh[ks], bUl[ks], acc);
+            if (n == C) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ob[ooff + (16 * tb + e) * rs] = acc[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (16 * tb + 4 * g4 + e < n) ob[ooff + (16 * tb + e) * rs] = acc[e];
+            }
+        }
+
+        // S0^T <- e^{G_n} S0^T + K^T diag(beta_t e^{G_n - G_t}) U, this wave's 64 columns
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) U[tb] *= *reinterpret_cast<const f32x4_t *>(gate + GATE_BW + 16 * tb + 4 * g4);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
+        const float eGn = gate[GATE_EGN];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            St[j] *= eGn;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                St[j] = mfma2b(colfrag(B.K, ks, 4 * hf + j, g4, lane), bUh[ks], bUl[ks], St[j]);
+        }
+        __syncthreads();  // A_{c+1}: chunk c + 1 is in the other buffer, and this one is free
+    }
+
+    float *dst = final_state + sbase;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4_t *>(dst + 16 * j + 4 * g4) = St[j];
+}
+
+hipError_t launch_chain_cs(const void *q, const void *k, const void *v, const int32_t *cu, const int32_t *chunk_base,
+                           const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H,
+                           const float *initial_state, float *o, float *final_state, const char *recs,
+                           hipStream_t stream) {
+    const int64_t units = n_seq * H;
+    const int64_t grid = ((units + 7) / 8) * 8 * CS_TILES;
+    hipLaunchKernelGGL(k_chunk_chain_cs, dim3((unsigned)grid), dim3(512), 0, stream,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                       static_cast<const uint16_t *>(v), cu, chunk_base, seq_order, (int)n_seq, total_tokens, H,
+                       initial_state, o, final_state, recs);
+    return hipGetLastError();
+}
+
 template <int NW>
 hipError_t launch_chain(const void *q, const void *k, const void *v, const int32_t *cu, const int32_t *chunk_base,
                         const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H,
@@ -620,6 +922,18 @@ int chain_waves(int64_t units) {
     if (forced == 2 || forced == 4) return forced;
     (void)units;
     return 4;  // measured faster than 2 even when 2 would fill more CUs (fewer record copies per head)
+}
+
+// The column-split chain (four workgroups per pair) when the (sequence, head)
+// pairs leave most CUs idle with two workgroups per pair; GDN_CHAIN_SPLIT=0|1
+// overrides (a tuning knob, read once).
+bool use_column_split(int64_t units) {
+    static const int forced = [] {
+        const char *e = getenv("GDN_CHAIN_SPLIT");
+        return e ? atoi(e) : -1;
+    }();
+    if (forced == 0 || forced == 1) return forced == 1;
+    return units * CS_TILES <= 256;
 }
 
 }  // namespace
@@ -652,14 +966,16 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     if (n_chunks > 0) {
         hipLaunchKernelGGL(k_chunk_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream,
                            static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), g, beta, cu_seqlens,
-                           chunk_base, (int)n_seq,
-                           total_tokens, H, recs);
+                           chunk_base, (int)n_seq, total_tokens, H, recs);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     e = record_mark(marks[1], stream);
     if (e != hipSuccess) return e;
-    if (chain_waves(n_seq * H) == 4)
+    if (use_column_split(n_seq * H))
+        e = launch_chain_cs(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
+                            final_state, recs, stream);
+    else if (chain_waves(n_seq * H) == 4)
         e = launch_chain<4>(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
                             final_state, recs, stream);
     else
