@@ -10,9 +10,12 @@ layers in "Layouts híbridos: três DeltaNet, uma attention", section Conceito),
 a 262,144-token context (same section), and 16,384-token segments (the
 training/cache plan in "attention and memory", "Sources, assumptions & limits").
 
-Recipe (every draw from numpy's PCG64 via ``default_rng``):
-  q, k, v     standard normal, float32, shape [N, H, d]; q and k are then
-              L2-normalised per (token, head) in float64
+Recipe (every draw from numpy's PCG64 via ``default_rng``; the tokens of a
+workload are drawn in blocks of BLOCK tokens, block b from child b of the
+workload's SeedSequence, so large workloads are generated on several threads
+with a result that does not depend on the thread count):
+  q, k, v     standard normal, float32, shape [n, H, d] per block; q and k are
+              then L2-normalised per (token, head) in float64
   beta        sigmoid of a standard normal logit
   g           exp(-softplus(x + shift)) of a standard normal logit x
               (shift 2 for the prefill/decode workloads, 0 for the single-head
@@ -33,11 +36,14 @@ SEED_BASE = 1000
 
 
 def bf16_round(x):
-    """Round float32 values to the nearest bfloat16 (ties to even); float32 out."""
+    """Round finite float32 values to the nearest bfloat16 (ties to even); float32 out."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    u = x.view(np.uint32)
+    r = (u >> 16) & 1          # no uint32 overflow for finite inputs (|bits| <= 0xFF7FFFFF)
+    r += 0x7FFF
+    r += u
+    r &= 0xFFFF0000
+    return r.view(np.float32)
 
 
 def bf16_bits(x):
@@ -59,10 +65,15 @@ def _gate_from_logit(x, shift):
 
 
 def _normalise(x):
-    x = x.astype(np.float64)
-    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
-    n[n == 0] = 1.0
-    return x / n
+    """L2-normalise the last axis in float64; float32 result (round to nearest)."""
+    out = np.empty(x.shape, dtype=np.float32)
+    step = 512
+    for i in range(0, x.shape[0], step):
+        xb = x[i:i + step].astype(np.float64)
+        n = np.sqrt(np.sum(xb * xb, axis=-1, keepdims=True))
+        n[n == 0] = 1.0
+        out[i:i + step] = xb / n
+    return out
 
 
 def _round_run_dtype(x64, dtype):
@@ -91,20 +102,54 @@ class PrefillInputs:
         return 1 if self.cu_seqlens is None else len(self.cu_seqlens) - 1
 
 
-def _draw_tokens(rng, N, H, dk, dv, dtype, gate_shift, unit_qk=True):
-    q = rng.standard_normal((N, H, dk), dtype=np.float32)
-    k = rng.standard_normal((N, H, dk), dtype=np.float32)
-    v = rng.standard_normal((N, H, dv), dtype=np.float32)
-    b_logit = rng.standard_normal((N, H), dtype=np.float32).astype(np.float64)
-    g_logit = rng.standard_normal((N, H), dtype=np.float32).astype(np.float64)
-    if unit_qk:
-        q = _normalise(q)
-        k = _normalise(k)
-    q = _round_run_dtype(q, dtype)
-    k = _round_run_dtype(k, dtype)
+BLOCK = 1024  # tokens per independent stream
+
+
+def _draw_block(ss, n, H, dk, dv, dtype, gate_shift):
+    rng = np.random.default_rng(ss)
+    q = rng.standard_normal((n, H, dk), dtype=np.float32)
+    k = rng.standard_normal((n, H, dk), dtype=np.float32)
+    v = rng.standard_normal((n, H, dv), dtype=np.float32)
+    b_logit = rng.standard_normal((n, H), dtype=np.float32).astype(np.float64)
+    g_logit = rng.standard_normal((n, H), dtype=np.float32).astype(np.float64)
+    q = _round_run_dtype(_normalise(q), dtype)
+    k = _round_run_dtype(_normalise(k), dtype)
     v = _round_run_dtype(v, dtype)
     beta = _sigmoid(b_logit).astype(np.float32)
     g = _gate_from_logit(g_logit, gate_shift).astype(np.float32)
+    return q, k, v, g, beta
+
+
+def _threads():
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _draw_tokens(ss, N, H, dk, dv, dtype, gate_shift):
+    """N tokens in blocks of BLOCK, block b from child b of SeedSequence ss."""
+    import concurrent.futures
+    nb = (N + BLOCK - 1) // BLOCK
+    children = ss.spawn(nb)
+    q = np.empty((N, H, dk), np.float32)
+    k = np.empty((N, H, dk), np.float32)
+    v = np.empty((N, H, dv), np.float32)
+    g = np.empty((N, H), np.float32)
+    beta = np.empty((N, H), np.float32)
+
+    def one(b):
+        a, e = b * BLOCK, min(N, (b + 1) * BLOCK)
+        q[a:e], k[a:e], v[a:e], g[a:e], beta[a:e] = _draw_block(children[b], e - a, H, dk, dv, dtype, gate_shift)
+
+    if nb <= 1:
+        for b in range(nb):
+            one(b)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(min(nb, _threads())) as ex:
+            list(ex.map(one, range(nb)))
     return q, k, v, g, beta
 
 
@@ -124,11 +169,12 @@ def make_prefill(lengths, H, d, dtype="bf16", seed=SEED_BASE, gate_shift=2.0,
     lengths = [int(x) for x in lengths]
     dv = d if dv is None else dv
     N = sum(lengths)
-    rng = np.random.default_rng(seed)
-    q, k, v, g, beta = _draw_tokens(rng, N, H, d, dv, dtype, gate_shift)
+    tok_ss, state_ss = np.random.SeedSequence(seed).spawn(2)
+    q, k, v, g, beta = _draw_tokens(tok_ss, N, H, d, dv, dtype, gate_shift)
     n = len(lengths)
     s_init = None
     if init_std is not None:
+        rng = np.random.default_rng(state_ss)
         s_init = (init_std * rng.standard_normal((n, H, dv, d), dtype=np.float32)).astype(np.float32)
     if packed is None:
         packed = n != 1
@@ -149,9 +195,9 @@ class DecodeInputs:
 
 
 def make_decode(steps, B, H, d, dtype="bf16", seed=SEED_BASE + 3, gate_shift=2.0, init_std=0.02):
-    rng = np.random.default_rng(seed)
-    q, k, v, g, beta = _draw_tokens(rng, steps * B, H, d, d, dtype, gate_shift)
-    s_init = (init_std * rng.standard_normal((B, H, d, d), dtype=np.float32)).astype(np.float32)
+    tok_ss, state_ss = np.random.SeedSequence(seed).spawn(2)
+    q, k, v, g, beta = _draw_tokens(tok_ss, steps * B, H, d, d, dtype, gate_shift)
+    s_init = (init_std * np.random.default_rng(state_ss).standard_normal((B, H, d, d), dtype=np.float32)).astype(np.float32)
     rs = lambda x: x.reshape((steps, B) + x.shape[1:])
     return DecodeInputs(rs(q), rs(k), rs(v), rs(g), rs(beta), s_init, dtype)
 
@@ -180,8 +226,7 @@ def config4_segments(n_seg=16, seg_len=16384, H=48, d=128):
     carried; segment i is drawn from child stream i of SeedSequence(1004)."""
     children = np.random.SeedSequence(SEED_BASE + 4).spawn(n_seg)
     for i, ss in enumerate(children):
-        rng = np.random.default_rng(ss)
-        q, k, v, g, beta = _draw_tokens(rng, seg_len, H, d, d, "bf16", 2.0)
+        q, k, v, g, beta = _draw_tokens(ss, seg_len, H, d, d, "bf16", 2.0)
         yield PrefillInputs(q, k, v, g, beta, None, None, "bf16",
                             meta=dict(segment=i, seg_len=seg_len, H=H, d=d))
 
@@ -198,9 +243,10 @@ def config5(H=48, d=128):
     sequences, per-sequence final states."""
     lengths = config5_lengths()
     _, data_ss = np.random.SeedSequence(SEED_BASE + 5).spawn(2)
-    rng = np.random.default_rng(data_ss)
+    tok_ss, state_ss = data_ss.spawn(2)
     N = sum(lengths)
-    q, k, v, g, beta = _draw_tokens(rng, N, H, d, d, "bf16", 2.0)
+    q, k, v, g, beta = _draw_tokens(tok_ss, N, H, d, d, "bf16", 2.0)
+    rng = np.random.default_rng(state_ss)
     s_init = (0.02 * rng.standard_normal((len(lengths), H, d, d), dtype=np.float32)).astype(np.float32)
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     return PrefillInputs(q, k, v, g, beta, cu, s_init, "bf16", meta=dict(lengths=lengths, H=H, d=d))

@@ -115,3 +115,96 @@ def test_config2_shape_slow_decay(oracle_lib):
     inp = w.config2(gate_shift=-4.0)
     inp.s_init = (0.02 * np.random.default_rng(5).standard_normal((1, 48, 128, 128))).astype(np.float32)
     check(inp, what="config2 slow decay")
+
+
+def test_many_pairs_use_the_two_workgroup_chain(oracle_lib):
+    """More than 64 (sequence, head) pairs: the chain with two workgroups per
+    pair (no column split), ragged lengths, nonzero initial states."""
+    say("72 pairs, varlen")
+    inp = w.make_prefill([300, 129, 64], H=24, d=128, seed=15, gate_shift=-1.0, init_std=0.2)
+    check(inp, what="72 pairs")
+
+
+def _head_slice(inp, heads):
+    """The same inputs restricted to some heads (for oracle runs on a sample)."""
+    return w.PrefillInputs(np.ascontiguousarray(inp.q[:, heads]), np.ascontiguousarray(inp.k[:, heads]),
+                           np.ascontiguousarray(inp.v[:, heads]), np.ascontiguousarray(inp.g[:, heads]),
+                           np.ascontiguousarray(inp.beta[:, heads]), inp.cu_seqlens,
+                           None if inp.s_init is None else np.ascontiguousarray(inp.s_init[:, heads]), inp.dtype)
+
+
+def test_config5_full_size(oracle_lib):
+    """8 packed sequences, log-uniform lengths in [1024, 65536] (130,093 tokens),
+    H=48, per-sequence initial states: oracle on four sampled heads, and the
+    token-serial GPU path on every head."""
+    say("config5 full size: generating")
+    inp = w.config5()
+    heads = [0, 17, 35, 47]
+    say("config5 full size: chunked prefill,", len(inp.meta["lengths"]), "sequences,", inp.q.shape[0], "tokens")
+    d = to_dev(inp)
+    o, s = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"], initial_state=d["s0"])
+    say("config5 full size: token-serial prefill")
+    o_ser, s_ser = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"], initial_state=d["s0"],
+                               chunk=gdn.CHUNK_SERIAL)
+    torch.cuda.synchronize()
+    rms_o = float(torch.sqrt(torch.mean(o_ser.double() ** 2)))
+    rms_s = float(torch.sqrt(torch.mean(s_ser.double() ** 2)))
+    e_o = float((o - o_ser).abs().max()) / rms_o
+    e_s = float((s - s_ser).abs().max()) / rms_s
+    say(f"config5 chunked vs token-serial (all heads): o={e_o:.2e} state={e_s:.2e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+    o_h = o[:, heads].cpu().numpy()
+    s_h = s[:, heads].cpu().numpy()
+    del d, o, s, o_ser, s_ser
+    say("config5 full size: oracle on heads", heads)
+    o_ref, s_ref = oracle_prefill(_head_slice(inp, heads))
+    eo, es = rel_max_err(o_h, o_ref), rel_max_err(s_h, s_ref)
+    say(f"config5 vs oracle (sampled heads): o={eo:.2e} state={es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_config4_segments_equal_one_shot(oracle_lib):
+    """262,144 tokens, H=48, as 16 segments of 16,384 with the fp32 state
+    carried, against one call over all tokens; the oracle (run segment by
+    segment, which is exact) on two sampled heads."""
+    heads = [5, 42]
+    qs, ks, vs, gs, bs, host = [], [], [], [], [], []
+    state = torch.zeros((1, 48, 128, 128), dtype=torch.float32, device=DEV)
+    o_seg = []
+    for seg in w.config4_segments():
+        i = seg.meta["segment"]
+        if i % 4 == 0:
+            say(f"config4: segment {i}")
+        d = to_dev(seg)
+        o, state = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=state, final_state=state)
+        o_seg.append(o)
+        qs.append(d["q"]); ks.append(d["k"]); vs.append(d["v"]); gs.append(d["g"]); bs.append(d["beta"])
+        host.append(_head_slice(seg, heads))
+    say("config4: one-shot call over 262,144 tokens")
+    q, k, v, g, b = (torch.cat(x) for x in (qs, ks, vs, gs, bs))
+    del qs, ks, vs, gs, bs
+    o_one, s_one = gdn.prefill(q, k, v, g, b)
+    torch.cuda.synchronize()
+    o_all = torch.cat(o_seg)
+    rms_o = float(torch.sqrt(torch.mean(o_one.double() ** 2)))
+    e_o = float((o_all - o_one).abs().max()) / rms_o
+    e_s = float((state - s_one).abs().max()) / float(torch.sqrt(torch.mean(s_one.double() ** 2)))
+    say(f"config4 segmented vs one-shot: o={e_o:.2e} state={e_s:.2e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+    o_h = o_all[:, heads].cpu().numpy()
+    s_h = state[:, heads].cpu().numpy()
+    del q, k, v, g, b, o_one, o_all, o_seg
+    say("config4: oracle on heads", heads, "segment by segment")
+    import oracle
+    s_ref = None
+    err_o, sq, n = 0.0, 0.0, 0
+    for i, seg in enumerate(host):
+        o_ref, s_ref = oracle.run(seg.q, seg.k, seg.v, seg.g, seg.beta, None, s_ref)
+        blk = o_h[i * 16384:(i + 1) * 16384]
+        err_o = max(err_o, float(np.max(np.abs(blk - o_ref))))
+        sq += float(np.sum(o_ref * o_ref))
+        n += o_ref.size
+    eo = err_o / np.sqrt(sq / n)
+    es = rel_max_err(s_h, s_ref)
+    say(f"config4 vs oracle (sampled heads): o={eo:.2e} state={es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
