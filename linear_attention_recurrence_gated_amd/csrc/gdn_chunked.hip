@@ -129,6 +129,17 @@ __device__ __forceinline__ void wait_all_vmem() {
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Workgroup barrier for waves whose LDS traffic must be complete (and visible)
+// at the barrier but whose global stores need not be: s_waitcnt lgkmcnt(0),
+// then s_barrier, with compiler memory barriers on both sides.  (A plain
+// __syncthreads() would also wait for the stores of o to reach memory.)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their no-wait maxima
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Row tiles in LDS.  Unit u (16 bytes, columns 8u..8u+7) of row t sits at
 // t * 256 + ((u ^ (t & 15)) << 4).
@@ -275,7 +286,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
         if (lane == 63) gate[GATE_EGN] = __expf(G63);
     }
     wait_all_vmem();
-    __syncthreads();
+    lds_barrier();
 
     // K K^T tiles (-> L) and P fragments, rows in natural column order
     for (int i = wave; i < 16; i += 4) {
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
                 u32x4_t{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
         }
     }
-    __syncthreads();  // L complete; Q no longer needed, its tile becomes T
+    lds_barrier();  // L complete; Q no longer needed, its tile becomes T
 
     // T = (I + L)^{-1} by 16x16 blocks.  Diagonal blocks D_a = (I + L_aa)^{-1}:
     // wave a, lane c solves column c by forward substitution from registers.
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
             for (int t = 0; t < 16; ++t) *tref(S.QT, 16 * a + t, 16 * a + 16 + c) = 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // Off-diagonal blocks, one level d = a - b at a time: Y = sum_{k=16b}^{16a-1} L[16a+i][k] T[k][16b+j],
     // then T_ab = -D_a Y.  Thread (i, j) = (tid >> 4, tid & 15) handles one element of each block.
     {
@@ -372,7 +383,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
                 }
                 S.Y[b][i][j] = acc;
             }
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int b = 0; b < 4 - d; ++b) {
                 const int a = b + d;
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
                 }
                 *tref(S.QT, 16 * a + i, 16 * b + j) = -acc;
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 
@@ -495,7 +506,7 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
     for (int jm = 0; jm < 8; ++jm)
         St[jm] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + 16 * jm + 4 * g4) : zero4();
 
-    __syncthreads();  // chunk 0 is in buf[0]
+    lds_barrier();  // chunk 0 is in buf[0]
     for (int c = 0; c < nc; ++c) {
         const int64_t t0 = seq_t0 + (int64_t)c * C;
         const int n = (int)min((int64_t)C, L - (int64_t)c * C);
@@ -585,7 +596,7 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) St[jm] = mfma2b(colfrag(B.K, ks, jm, g4, lane), bUh[ks], bUl[ks], St[jm]);
         }
-        __syncthreads();  // chunk c + 1 is in the other buffer, and this one is free
+        lds_barrier();  // chunk c + 1 is in the other buffer, and this one is free
     }
 
     float *dst = final_state + sbase;
@@ -643,36 +654,41 @@ __device__ __forceinline__ u32x4_t vfrag(const char *tile, int ks, int col0, int
     return u32x4_t{a2[0], a2[1], b2[0], b2[1]};
 }
 
-// Copies of one chunk, 16 global->LDS loads per copy wave (the vmcnt waits
-// below rely on that count being the same for every wave): wave 0 copies
+// Copies of one chunk, 16 global->LDS loads per copy wave in two halves of 8
+// (the vmcnt waits below rely on those counts being the same for every wave): wave 0 copies
 // record kilobytes 0..15, wave 1 record kilobytes 16..24, the four of the v
 // columns and three padding loads (record kilobyte 0 into a scratch
 // kilobyte), wave 2 the q rows and wave 3 the k rows.  Every wave therefore
 // has exactly 16 loads in flight after its copies.
 static_assert(REC_PIECES == 25 && VC_BYTES / FRAG == 4, "copy assignment");
 __device__ __forceinline__ void cs_copies(ChainBufCS &B, char *scratch, const char *rec, const uint16_t *qc,
-                                          const uint16_t *kc, const uint16_t *vc, int rs, int n, int lane, int cw) {
+                                          const uint16_t *kc, const uint16_t *vc, int rs, int n, int lane, int cw,
+                                          int half) {
+    const int a0 = 8 * half, a1 = a0 + 8;  // loads a0 .. a1 - 1 of this wave's 16
     if (cw == 0) {
 #pragma unroll
-        for (int a = 0; a < 16; ++a)
+        for (int a = a0; a < a1; ++a)
             __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + a * FRAG + lane * 16),
                                              (lds_void *)(B.rec + a * FRAG), 16, 0, 0);
     } else if (cw == 1) {
+        // record kilobytes 16..24 are loads 0..8, the v columns loads 9..12, padding 13..15
 #pragma unroll
-        for (int a = 16; a < REC_PIECES; ++a)
-            __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + a * FRAG + lane * 16),
-                                             (lds_void *)(B.rec + a * FRAG), 16, 0, 0);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) dma_vcols(B.V, vc, rs, n, lane, a);
-#pragma unroll
-        for (int a = 0; a < 16 - (REC_PIECES - 16) - 4; ++a)
-            __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + lane * 16), (lds_void *)scratch, 16, 0,
-                                             0);
+        for (int a = a0; a < a1; ++a) {
+            if (a < REC_PIECES - 16) {
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + (16 + a) * FRAG + lane * 16),
+                                                 (lds_void *)(B.rec + (16 + a) * FRAG), 16, 0, 0);
+            } else if (a < REC_PIECES - 16 + 4) {
+                dma_vcols(B.V, vc, rs, n, lane, a - (REC_PIECES - 16));
+            } else {
+                __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + lane * 16), (lds_void *)scratch, 16, 0,
+                                                 0);
+            }
+        }
     } else {
         const uint16_t *src = cw == 2 ? qc : kc;
         char *dst = cw == 2 ? B.Q : B.K;
 #pragma unroll
-        for (int a = 0; a < 16; ++a) dma_row_piece(dst, src, rs, n, lane, a);
+        for (int a = a0; a < a1; ++a) dma_row_piece(dst, src, rs, n, lane, a);
     }
 }
 
@@ -717,12 +733,12 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
 
     if (wave >= 4) {  // copy wave
         const int cw = wave - 4;
-        auto copies = [=](int c) {
+        auto copies = [=](int c, int half) {
             const int64_t t0 = seq_t0 + (int64_t)c * C;
             const int n = (int)min((int64_t)C, L - (int64_t)c * C);
             const int64_t rowbase = (t0 * H + h) * DK;
             cs_copies(sm.buf[c & 1], sm.scratch, recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q + rowbase,
-                      k + rowbase, v + rowbase + vcol0, rs, n, lane, cw);
+                      k + rowbase, v + rowbase + vcol0, rs, n, lane, cw, half);
         };
         // Touch chunk c: the first 16 bytes of each 128-byte line in this
         // workgroup's quarter of the lines (the four workgroups of a pair share
@@ -739,21 +755,28 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)sm.scratch, 16, 0, 0);
         };
         // Barriers: A_0, then per chunk c: X_c, A_{c+1}.  Chunk c + 1 is
-        // copied between X_c and A_{c+1} (its buffer, last used for chunk
-        // c - 1, is free since A_c), so issuing the copies never holds up the
-        // compute waves' exchange at X_c.  These waves make no other LDS
-        // accesses, and their copies are complete once vmcnt says so, so their
-        // barriers are bare (no wait for the touch in flight).
-        if (nc > 0) copies(0);
+        // copied between A_c (its buffer, last used for chunk c - 1, is free
+        // from then on) and A_{c+1}: half before X_c, while the compute waves
+        // form their partial products, and half after, so that issuing the
+        // copies does not hold up the exchange at X_c for long.  These waves
+        // make no other LDS accesses, and their copies are complete once
+        // vmcnt says so, so their barriers are bare (no wait for the touch in
+        // flight).
+        if (nc > 0) {
+            copies(0, 0);
+            copies(0, 1);
+        }
         for (int c = 1; c < PF_DIST && c < nc; ++c) touch(c);
         wait_all_vmem();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // A_0
         for (int c = 0; c < nc; ++c) {
             asm volatile("" ::: "memory");
+            if (c + 1 < nc) copies(c + 1, 0);
+            asm volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();  // X_c
             asm volatile("" ::: "memory");
-            if (c + 1 < nc) copies(c + 1);
+            if (c + 1 < nc) copies(c + 1, 1);
             if (c + PF_DIST < nc) {
                 touch(c + PF_DIST);  // issued after every copy of this iteration
                 __builtin_amdgcn_s_waitcnt(0x0F71);  // vmcnt(1): everything but the newest touch has landed
@@ -777,7 +800,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     // output tiles of this wave: {0, 3} or {1, 2} (balanced P U work)
     const int ta = hf ? 1 : 0, tz = hf ? 2 : 3;
 
-    __syncthreads();  // A_0: chunk 0 is in buf[0]
+    lds_barrier();  // A_0: chunk 0 is in buf[0]
     for (int c = 0; c < nc; ++c) {
         const int64_t t0 = seq_t0 + (int64_t)c * C;
         const int n = (int)min((int64_t)C, L - (int64_t)c * C);
@@ -805,11 +828,12 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             sm.xch[wave][tb][lane] = X[tb];
             sm.xch[wave][4 + tb][lane] = O[tb];
         }
-        __syncthreads();  // X_c: partials visible
+        lds_barrier();  // X_c: partials visible
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) X[tb] += sm.xch[wave ^ 1][tb][lane];
-        O[ta] += sm.xch[wave ^ 1][4 + ta][lane];
-        O[tz] += sm.xch[wave ^ 1][4 + tz][lane];
+        for (int tb = 0; tb < 4; ++tb) {
+            X[tb] += sm.xch[wave ^ 1][tb][lane];
+            if (tb == ta || tb == tz) O[tb] += sm.xch[wave ^ 1][4 + tb][lane];  // static indices, uniform test
+        }
 
         // Y = V - diag(e^{G_{t-1}}) X
         u32x4_t bYh[2], bYl[2];
@@ -844,8 +868,8 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         float *ob = o + t0 * rs + h * DK;
         const int ooff = 4 * g4 * rs + iw + r;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tb = i ? tz : ta;
+        for (int tb = 0; tb < 4; ++tb) {
+            if (tb != ta && tb != tz) continue;  // uniform; keeps O[] indices static
             f32x4_t acc = O[tb] * *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * tb + 4 * g4);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
@@ -874,7 +898,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             for (int ks = 0; ks < 2; ++ks)
                 St[j] = mfma2b(colfrag(B.K, ks, 4 * hf + j, g4, lane), bUh[ks], bUl[ks], St[j]);
         }
-        __syncthreads();  // A_{c+1}: chunk c + 1 is in the other buffer, and this one is free
+        lds_barrier();  // A_{c+1}: chunk c + 1 is in the other buffer, and this one is free
     }
 
     float *dst = final_state + sbase;
