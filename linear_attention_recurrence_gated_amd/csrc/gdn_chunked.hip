@@ -233,14 +233,14 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t *__restrict__ cu, in
 // k_chunk_prep: one 4-wave workgroup per (global chunk, head).
 
 struct PrepSmem {
-    __attribute__((aligned(16))) char K[TILE];   // row tiles of the chunk
-    __attribute__((aligned(16))) char QT[TILE];  // Q while P is formed, then T (fp32, swizzled 16-byte units)
-    float L[64][68];                             // L (strictly lower triangular)
-    float Y[3][16][16];                          // per-level block products
+    __attribute__((aligned(16))) char KL[TILE];  // row tile of k, then L (fp32, swizzled as T)
+    __attribute__((aligned(16))) char QT[TILE];  // row tile of q while P is formed, then T (fp32, swizzled)
+    float scr[32 * 36];                          // products of the inverse's doubling steps
     float G[64], B[64];
 };
 
-// T[t][s] in the QT region: 16-byte unit (s >> 2) of row t XOR-swizzled by (t & 15).
+// T[t][s] (and L[t][s]) in a 64 x 64 fp32 tile: 16-byte unit (s >> 2) of row t
+// XOR-swizzled by (t & 15).
 __device__ __forceinline__ float *tref(char *qt, int t, int s) {
     return reinterpret_cast<float *>(qt + t * 256 + ((((s >> 2) ^ (t & 15)) << 4)) + (s & 3) * 4);
 }
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
     __shared__ PrepSmem S;
 
     // q, k rows of the chunk -> LDS row tiles (8 one-kilobyte copies per wave)
-    dma_rows(S.K, k + cbase, rs, n, lane, wave, 4);
+    dma_rows(S.KL, k + cbase, rs, n, lane, wave, 4);
     dma_rows(S.QT, q + cbase, rs, n, lane, wave, 4);
     if (wave == 0) {  // gate prefix sums and the record's gate factors
         const int64_t off = (t0 + min(lane, n - 1)) * H + h;
@@ -288,24 +288,30 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
     wait_all_vmem();
     lds_barrier();
 
-    // K K^T tiles (-> L) and P fragments, rows in natural column order
-    for (int i = wave; i < 16; i += 4) {
+    // K K^T tiles (the 10 tiles on and below the diagonal; item i = wave + 4 j,
+    // i < 10, kept in registers until k's tile may be overwritten) and the P
+    // fragments (items 10..15, straight to the record).
+    f32x4_t Lr[3];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = wave + 4 * j;
         if (i < 10) {
             const int ta = i >= 6 ? 3 : i >= 3 ? 2 : i >= 1 ? 1 : 0;
             const int sa = i - ta * (ta + 1) / 2;
             f32x4_t acc = zero4();
 #pragma unroll
             for (int kj = 0; kj < 4; ++kj)
-                acc = mfma(rowfrag(S.K, 16 * ta, kj, g4, r), rowfrag(S.K, 16 * sa, kj, g4, r), acc);
+                acc = mfma(rowfrag(S.KL, 16 * ta, kj, g4, r), rowfrag(S.KL, 16 * sa, kj, g4, r), acc);
             const int s = 16 * sa + r;
             const float gs = S.G[s], bs = S.B[s];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * ta + 4 * g4 + e;
                 const float gtm1 = t > 0 ? S.G[t - 1] : 0.f;
-                S.L[t][s] = (s < t) ? bs * __expf(gtm1 - gs) * acc[e] : 0.f;
+                acc[e] = (s < t) ? bs * __expf(gtm1 - gs) * acc[e] : 0.f;
             }
-        } else {
+            if (j < 3) Lr[j] = acc;
+        } else if (i < 16) {
             const int pb = i - 10;  // P fragment tblk(tb, ks)
             const int tb = pb < 2 ? pb : 2 + ((pb - 2) >> 1), ks = pb < 2 ? 0 : ((pb - 2) & 1);
             u32x2_t hi[2], lo[2];
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
                     f32x4_t acc = zero4();
 #pragma unroll
                     for (int kj = 0; kj < 4; ++kj)
-                        acc = mfma(rowfrag(S.K, 16 * sa, kj, g4, r), rowfrag(S.QT, 16 * tb, kj, g4, r), acc);
+                        acc = mfma(rowfrag(S.KL, 16 * sa, kj, g4, r), rowfrag(S.QT, 16 * tb, kj, g4, r), acc);
                     const int t = 16 * tb + r;
                     const float Gt = S.G[t];
 #pragma unroll
@@ -334,7 +340,18 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
                 u32x4_t{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
         }
     }
-    lds_barrier();  // L complete; Q no longer needed, its tile becomes T
+    lds_barrier();  // k and q are no longer needed: their tiles become L and T
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int i = wave + 4 * j;
+        if (i < 10) {
+            const int ta = i >= 6 ? 3 : i >= 3 ? 2 : i >= 1 ? 1 : 0;
+            const int sa = i - ta * (ta + 1) / 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *tref(S.KL, 16 * ta + 4 * g4 + e, 16 * sa + r) = Lr[j][e];
+        }
+    }
+    lds_barrier();  // L complete
 
     // T = (I + L)^{-1} by 16x16 blocks.  Diagonal blocks D_a = (I + L_aa)^{-1}:
     // wave a, lane c solves column c by forward substitution from registers.
@@ -345,7 +362,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
         for (int t = 1; t < 16; ++t)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 x = *reinterpret_cast<const float4 *>(&S.L[16 * a + t][16 * a + 4 * q4]);
+                const float4 x = t4(S.KL, 16 * a + t, 16 * a + 4 * q4);
                 lb[t][4 * q4] = x.x; lb[t][4 * q4 + 1] = x.y; lb[t][4 * q4 + 2] = x.z; lb[t][4 * q4 + 3] = x.w;
             }
         float x[16];
@@ -365,39 +382,53 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
         }
     }
     lds_barrier();
-    // Off-diagonal blocks, one level d = a - b at a time: Y = sum_{k=16b}^{16a-1} L[16a+i][k] T[k][16b+j],
-    // then T_ab = -D_a Y.  Thread (i, j) = (tid >> 4, tid & 15) handles one element of each block.
+    // Off-diagonal blocks by doubling, on fp32 MFMA (v_mfma_f32_16x16x4f32:
+    // lane (g, r) holds A[r][g] and B[g][r]; the result tile is laid out as in
+    // the bf16 MFMA).  With T_A, T_B the inverses of the top-left and
+    // bottom-right 32x32 parts:
+    //   T10 = -D1 (L10 D0),  T32 = -D3 (L32 D2)                  (waves 0, 1)
+    //   Z   = L[32:64][0:32] T_A                                  (4 waves, one 16x16 tile each)
+    //   T[32:64][0:32] = -T_B Z                                   (4 waves)
     {
-        const int i = tid >> 4, j = tid & 15;
+        float *scr = S.scr;  // M: [2][16][16], then Z: [32][36]
+        if (wave < 2) {
+            const int ab = 2 * wave, aa = ab + 1;  // T_{aa, ab}
+            f32x4_t m = zero4();
 #pragma unroll
-        for (int d = 1; d <= 3; ++d) {
+            for (int st = 0; st < 4; ++st)
+                m = __builtin_amdgcn_mfma_f32_16x16x4f32(*tref(S.KL, 16 * aa + r, 16 * ab + 4 * st + g4),
+                                                         *tref(S.QT, 16 * ab + 4 * st + g4, 16 * ab + r), m, 0, 0, 0);
+            float *mw = scr + wave * 256;
 #pragma unroll
-            for (int b = 0; b < 4 - d; ++b) {
-                const int a = b + d;
-                float acc = 0.f;
+            for (int e = 0; e < 4; ++e) mw[(4 * g4 + e) * 16 + r] = m[e];  // this wave reads it back (LDS is in order)
+            f32x4_t t = zero4();
 #pragma unroll
-                for (int kk = 16 * b; kk < 16 * a; kk += 4) {
-                    const float4 l4 = *reinterpret_cast<const float4 *>(&S.L[16 * a + i][kk]);
-                    acc += l4.x * *tref(S.QT, kk, 16 * b + j) + l4.y * *tref(S.QT, kk + 1, 16 * b + j) +
-                           l4.z * *tref(S.QT, kk + 2, 16 * b + j) + l4.w * *tref(S.QT, kk + 3, 16 * b + j);
-                }
-                S.Y[b][i][j] = acc;
-            }
-            lds_barrier();
+            for (int st = 0; st < 4; ++st)
+                t = __builtin_amdgcn_mfma_f32_16x16x4f32(*tref(S.QT, 16 * aa + r, 16 * aa + 4 * st + g4),
+                                                         mw[(4 * st + g4) * 16 + r], t, 0, 0, 0);
 #pragma unroll
-            for (int b = 0; b < 4 - d; ++b) {
-                const int a = b + d;
-                float acc = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < 16; kk += 4) {
-                    const float4 d4 = t4(S.QT, 16 * a + i, 16 * a + kk);
-                    acc += d4.x * S.Y[b][kk][j] + d4.y * S.Y[b][kk + 1][j] + d4.z * S.Y[b][kk + 2][j] +
-                           d4.w * S.Y[b][kk + 3][j];
-                }
-                *tref(S.QT, 16 * a + i, 16 * b + j) = -acc;
-            }
-            lds_barrier();
+            for (int e = 0; e < 4; ++e) *tref(S.QT, 16 * aa + 4 * g4 + e, 16 * ab + r) = -t[e];
         }
+        lds_barrier();
+        const int ti = wave >> 1, tj = wave & 1;
+        {
+            f32x4_t z = zero4();
+            for (int k4 = tj ? 4 : 0; k4 < 8; ++k4)  // T_A[k][16 tj + c] is zero for k < 16 tj
+                z = __builtin_amdgcn_mfma_f32_16x16x4f32(*tref(S.KL, 32 + 16 * ti + r, 4 * k4 + g4),
+                                                         *tref(S.QT, 4 * k4 + g4, 16 * tj + r), z, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) scr[(16 * ti + 4 * g4 + e) * 36 + 16 * tj + r] = z[e];
+        }
+        lds_barrier();
+        {
+            f32x4_t t = zero4();
+            for (int k4 = 0; k4 < (ti ? 8 : 4); ++k4)  // T_B[16 ti + r][k] is zero for k >= 16 (ti + 1)
+                t = __builtin_amdgcn_mfma_f32_16x16x4f32(*tref(S.QT, 32 + 16 * ti + r, 32 + 4 * k4 + g4),
+                                                         scr[(4 * k4 + g4) * 36 + 16 * tj + r], t, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *tref(S.QT, 32 + 16 * ti + 4 * g4 + e, 16 * tj + r) = -t[e];
+        }
+        lds_barrier();
     }
 
     // T fragments: block tblk(tb, ks), lane (g, r) holds T[16 tb + r][32 ks + slot_k(g, e)], split hi/lo
