@@ -18,6 +18,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdn_oracle.so")
+PRE_LIB_PATH = os.path.join(HERE, "libgdn_preprocess.so")
 
 _libs = {}
 
@@ -108,3 +109,58 @@ def run_decode(q, k, v, g, beta, s_init, threads=None, lib_path=LIB_PATH):
     o, s = run(pack(q), pack(k), pack(v), pack(g), pack(beta), cu, s_init, threads, lib_path)
     o = np.swapaxes(o.reshape(B, steps, H, dv), 0, 1)
     return o, s
+
+
+def _load_pre(path=PRE_LIB_PATH):
+    lib = _libs.get(path)
+    if lib is not None:
+        return lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"oracle library {path} is not built; run oracle/build.py")
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int64)
+    lib.gdn_oracle_preprocess.restype = ctypes.c_int
+    lib.gdn_oracle_preprocess.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ip, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_int, dp, dp, dp, dp, dp, dp]
+    _libs[path] = lib
+    return lib
+
+
+def preprocess(xq, xk, xv, w, a_logit, b_logit, bias=None, cu_seqlens=None, state_in=None, activation="none",
+               lib_path=PRE_LIB_PATH):
+    """Pre-processing in front of the recurrence (gdn_preprocess.c): causal
+    depthwise 4-tap convolution of q, k, v with a per-sequence conv state,
+    optional SiLU, per-(token, head) L2 normalisation of q and k, and the gate
+    maps beta = sigmoid(b), g = exp(-softplus(a + bias)).
+
+    xq, xk, xv: [N, H, d]; w: [3, H, d, 4]; a_logit, b_logit: [N, H]; bias: [H]
+    or None; cu_seqlens: [n_seq + 1] or None; state_in: [n_seq, 3, 3, H, d] or
+    None (zeros).  Returns (q, k, v, g, beta, state_out) as float64.
+    """
+    xq, xk, xv, w, a, b = (_f64(x) for x in (xq, xk, xv, w, a_logit, b_logit))
+    N, H, d = xq.shape
+    assert xk.shape == xq.shape and xv.shape == xq.shape and w.shape == (3, H, d, 4)
+    assert a.shape == (N, H) and b.shape == (N, H)
+    if cu_seqlens is None:
+        cu, n_seq = None, 1
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        n_seq = cu.shape[0] - 1
+    bias64 = None if bias is None else _f64(bias)
+    st = None if state_in is None else _f64(state_in)
+    if st is not None:
+        assert st.shape == (n_seq, 3, 3, H, d)
+    act = {"none": 0, "silu": 1}[activation]
+    yq, yk, yv = (np.zeros((N, H, d)) for _ in range(3))
+    g = np.zeros((N, H))
+    beta = np.zeros((N, H))
+    st_out = np.zeros((n_seq, 3, 3, H, d))
+    lib = _load_pre(lib_path)
+    cu_ptr = None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    rc = lib.gdn_oracle_preprocess(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(w), _ptr(st), _ptr(a), _ptr(b), _ptr(bias64),
+                                   cu_ptr, n_seq, N, H, d, act, _ptr(yq), _ptr(yk), _ptr(yv), _ptr(g), _ptr(beta),
+                                   _ptr(st_out))
+    if rc != 0:
+        raise ValueError(f"gdn_oracle_preprocess rejected its arguments (code {rc})")
+    return yq, yk, yv, g, beta, st_out
