@@ -43,6 +43,9 @@ PREFILL_FLOP_FULL_PER_TOKEN_HEAD = 5 * 2 * C * D + 3 * 2 * D * D                
 PREP_FLOP_PER_TOKEN_HEAD = (C - 1) * D + (C + 1) * D + 2 * (C - 1) * D             # K K^T, Q K^T, W, U~ = 32,512
 CHAIN_FLOP_PER_TOKEN_HEAD = PREFILL_FLOP_PER_TOKEN_HEAD - PREP_FLOP_PER_TOKEN_HEAD  # 106,624
 DECODE_BYTES_PER_HEAD_TOKEN = 2 * STATE_BYTES_PER_HEAD + 3 * D * 2 + 2 * 4 + D * 4  # 132,360
+# pre-processing: raw q, k, v in (bf16) + two logits, q, k, v out (bf16) + g, beta
+PRE_BYTES_PER_TOKEN_HEAD = 2 * (3 * D * 2 + 2 * 4)                                  # 1,552
+PRE_BYTES_FIXED = 3 * H * D * 4 * 4 + 2 * 9 * H * D * 2                              # taps + conv state in/out
 
 
 def source_hash():
@@ -175,6 +178,39 @@ def bench_decode(torch, gdn, w, steps, rotate):
     return ms
 
 
+def bench_preprocess(torch, gdn, w, steps, warmup, rotate):
+    """gdn_preprocess over the one-layer prefill shape (T = 4096, H = 48,
+    d = 128, bf16, SiLU, with conv state and gate bias); successive calls cycle
+    over `rotate` resident copies of the inputs."""
+    inp = w.make_preprocess([T], H=H, d=D, dtype="bf16", seed=w.SEED_BASE + 6, activation="silu", packed=False)
+    dev = "cuda:0"
+    f = lambda x: torch.from_numpy(x).to(dev)
+    bf = lambda x: w.to_torch(x, "bf16", dev)
+    sets = [dict(xq=bf(inp.xq), xk=bf(inp.xk), xv=bf(inp.xv), a=f(inp.a_logit), b=f(inp.b_logit),
+                 st=bf(inp.state_in)) for _ in range(rotate)]
+    wt, bias = f(inp.w), f(inp.bias)
+    outs = [(torch.empty_like(s["xq"]), torch.empty_like(s["xk"]), torch.empty_like(s["xv"]),
+             torch.empty((T, H), dtype=torch.float32, device=dev), torch.empty((T, H), dtype=torch.float32, device=dev))
+            for s in sets]
+    st_out = [torch.empty_like(s["st"]) for s in sets]
+
+    def call(i):
+        s = sets[i % rotate]
+        gdn.preprocess(s["xq"], s["xk"], s["xv"], wt, s["a"], s["b"], gate_bias=bias, conv_state_in=s["st"],
+                       conv_state_out=st_out[i % rotate], activation="silu", out=outs[i % rotate])
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        call(i)
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
+
+
 def bench_copy(torch, gdn, mib, reps):
     """Calibration run for the HBM byte counters: gdn_state_init copying a
     state of about `mib` MiB (k_state_fill reads and writes each byte once)."""
@@ -226,6 +262,17 @@ def cpu_baseline(w, seconds):
             "gflops": runs * T * H * 6 * D * D / el / 1e9}
 
 
+def pre_entry(pre_ms):
+    """Pre-processing (convolution, SiLU, norm, gate maps) at T = 4096, H = 48."""
+    nbytes = PRE_BYTES_PER_TOKEN_HEAD * T * H + PRE_BYTES_FIXED
+    ms = mean(pre_ms)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"mean_ms": ms, "p50_ms": pct(pre_ms, 50), "tokens_per_s_layer": T / (ms / 1e3),
+            "roofline": {"kernel": "k_preprocess + k_conv_state (one gdn_preprocess call)", "bound": "hbm",
+                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "algorithmic_bytes": nbytes, "traffic": load_traffic("k_preprocess")}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,7 +282,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of parts to time alone (prefill, decode, copy), one JSON line each, for "
+                    help="comma list of parts to time alone (prefill, decode, preprocess, copy), one JSON line each, for "
                          "profiling runs; 'copy' is the byte-counter calibration copy")
     ap.add_argument("--warm", action="store_true",
                     help="also time one resident copy (inputs and state may then sit in the last-level cache)")
@@ -258,7 +305,7 @@ def main():
 
     if args.only:
         parts = args.only.split(",")
-        bad = [p for p in parts if p not in ("prefill", "decode", "copy")]
+        bad = [p for p in parts if p not in ("prefill", "decode", "preprocess", "copy")]
         if bad:
             ap.error(f"--only: unknown part(s) {bad}")
         for part in parts:
@@ -269,11 +316,15 @@ def main():
             elif part == "decode":
                 dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
                 print(json.dumps({"only": "decode", "ms_per_step": mean(dec_ms)}), flush=True)
+            elif part == "preprocess":
+                pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
+                print(json.dumps({"only": "preprocess", "ms_per_call": mean(pre_ms)}), flush=True)
             else:
                 print(json.dumps(bench_copy(torch, gdn, args.copy_mib, max(1, args.steps))), flush=True)
         return
     ms, ms_call, wall = bench_prefill(torch, gdn, w, args.steps, args.warmup, args.rotate)
     dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
+    pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
 
     step_ms = mean(ms)
     tok_s = T / (step_ms / 1e3)
@@ -336,6 +387,7 @@ def main():
                    "roofline": {"kernel": "k_decode_step", "bound": "hbm", "achieved": dec_gbs,
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                                 "traffic": load_traffic("k_decode_step")}},
+        "preprocess": pre_entry(pre_ms),
         "rotate": args.rotate,
         "conditions": run_conditions(torch),
     }

@@ -134,6 +134,46 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtyp
                            const float *g, const float *beta, float *state, float *o,
                            int64_t B, int32_t H, int32_t dk, int32_t dv, void *stream);
 
+/* Activation after the pre-processing convolution. */
+typedef enum { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_activation;
+
+/* Pre-processing in front of the recurrence, for a packed batch laid out as
+ * for gdn_prefill.  The DeltaNet layers of "Layouts híbridos: três DeltaNet,
+ * uma attention" (llmdeepdive.com), section Conceito, carry a convolution of
+ * kernel 4 beside their gated state; "Qwen3.8-27B 架构深读"
+ * (feifeigd.github.io, 2026-08-17), section 三, gives one gate and one write
+ * strength per token.  Per sequence, head and channel of each of q, k, v:
+ *   y_t = w[0] x_{t-3} + w[1] x_{t-2} + w[2] x_{t-1} + w[3] x_t
+ * (causal, depthwise; before a sequence's first token the window holds the
+ * sequence's conv state), then SiLU when activation == GDN_ACT_SILU; q and k
+ * are L2-normalised per (token, head) (a zero vector stays zero), v is not;
+ *   beta = sigmoid(b_logit),  g = exp(-softplus(a_logit + gate_bias[h])).
+ *
+ *   xq, xk, xv       [N][H][d] dtype: raw (projected) q, k, v
+ *   conv_w           [3][H][d][4] fp32: taps of tensor q, k, v (tap 3 = current token)
+ *   conv_state_in    [n_seq][3][3][H][d] dtype: per sequence and tensor, the raw
+ *                    inputs of the three tokens before this part (oldest first),
+ *                    or NULL for zeros
+ *   conv_state_out   [n_seq][3][3][H][d] dtype: the last three raw inputs of each
+ *                    sequence (for a sequence shorter than three, shifted in from
+ *                    its starting state).  May be the same pointer as
+ *                    conv_state_in (updated in place), but may not otherwise
+ *                    overlap it.  Feeding it back as the next part's
+ *                    conv_state_in continues the sequence exactly.
+ *   a_logit, b_logit [N][H] fp32;   gate_bias [H] fp32 or NULL (zeros)
+ *   cu_seqlens, cu_seqlens_host, n_seq, total_tokens: as for gdn_prefill
+ *   q, k, v          [N][H][d] dtype outputs (rounded to nearest even for bf16);
+ *                    they may not overlap any input
+ *   g, beta          [N][H] fp32 outputs
+ * A decode step is a batch of n_seq one-token sequences.  Errors as for the
+ * other calls; activation outside the enum is GDN_ERR_UNSUPPORTED. */
+gdn_status gdn_preprocess(const void *xq, const void *xk, const void *xv, gdn_dtype dtype,
+                          const float *conv_w, const void *conv_state_in, void *conv_state_out,
+                          const float *a_logit, const float *b_logit, const float *gate_bias,
+                          const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
+                          int64_t total_tokens, int32_t H, int32_t d, int32_t activation,
+                          void *q, void *k, void *v, float *g, float *beta, void *stream);
+
 /* Profiling hook.  Arms up to three caller-owned hipEvent_t handles
  * (events[0..n_events-1]; NULL entries are skipped) for the NEXT gdn_prefill
  * call made by this host thread, which records them on its stream:

@@ -272,4 +272,63 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtyp
                       "decode_step launch");
 }
 
+gdn_status gdn_preprocess(const void *xq, const void *xk, const void *xv, gdn_dtype dtype, const float *conv_w,
+                          const void *conv_state_in, void *conv_state_out, const float *a_logit,
+                          const float *b_logit, const float *gate_bias, const int32_t *cu_seqlens,
+                          const int32_t *cu_seqlens_host, int64_t n_seq, int64_t total_tokens, int32_t H, int32_t d,
+                          int32_t activation, void *q, void *k, void *v, float *g, float *beta, void *stream) {
+    if (dtype != GDN_BF16 && dtype != GDN_FP32) return fail(GDN_ERR_DTYPE, "preprocess: dtype %d", (int)dtype);
+    if (n_seq < 0 || total_tokens < 0 || H <= 0 || total_tokens * (int64_t)H > (int64_t)INT32_MAX * 16)
+        return fail(GDN_ERR_SHAPE, "preprocess: n_seq=%lld total_tokens=%lld H=%d", (long long)n_seq,
+                    (long long)total_tokens, H);
+    if (!supported_d(d, d)) return fail(GDN_ERR_UNSUPPORTED, "preprocess: d=%d not supported", d);
+    if (activation != GDN_ACT_NONE && activation != GDN_ACT_SILU)
+        return fail(GDN_ERR_UNSUPPORTED, "preprocess: activation %d", activation);
+    if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr))
+        return fail(GDN_ERR_NULL, "preprocess: cu_seqlens and cu_seqlens_host must both be given or both be NULL");
+    if (!cu_seqlens_host) {
+        if (n_seq != 1) return fail(GDN_ERR_SEQLENS, "preprocess: without cu_seqlens n_seq must be 1 (got %lld)",
+                                    (long long)n_seq);
+    } else {
+        if (!aligned(cu_seqlens, 4)) return fail(GDN_ERR_ALIGN, "preprocess: cu_seqlens must be 4-byte aligned");
+        if (cu_seqlens_host[0] != 0) return fail(GDN_ERR_SEQLENS, "preprocess: cu_seqlens[0] = %d", cu_seqlens_host[0]);
+        for (int64_t s = 0; s < n_seq; ++s)
+            if (cu_seqlens_host[s + 1] < cu_seqlens_host[s])
+                return fail(GDN_ERR_SEQLENS, "preprocess: cu_seqlens decreases at %lld", (long long)s);
+        if (cu_seqlens_host[n_seq] != total_tokens)
+            return fail(GDN_ERR_SEQLENS, "preprocess: cu_seqlens[n_seq] = %d but total_tokens = %lld",
+                        cu_seqlens_host[n_seq], (long long)total_tokens);
+    }
+    if (n_seq == 0) return ok();
+    if (!conv_state_out) return fail(GDN_ERR_NULL, "preprocess: conv_state_out is NULL");
+    if (total_tokens > 0 && (!xq || !xk || !xv || !conv_w || !a_logit || !b_logit || !q || !k || !v || !g || !beta))
+        return fail(GDN_ERR_NULL, "preprocess: inputs and outputs are required when total_tokens > 0");
+    const size_t eb = elem_bytes(dtype), NH = (size_t)total_tokens * H, sb = (size_t)n_seq * 9 * H * d * eb;
+    for (const void *p : {xq, xk, xv, (const void *)q, (const void *)k, (const void *)v, conv_state_in,
+                          (const void *)conv_state_out, (const void *)conv_w})
+        if (p && !aligned(p, 16)) return fail(GDN_ERR_ALIGN, "preprocess: tensors and conv states must be 16-byte aligned");
+    if (!aligned(a_logit, 4) || !aligned(b_logit, 4) || !aligned(gate_bias, 4) || !aligned(g, 4) || !aligned(beta, 4))
+        return fail(GDN_ERR_ALIGN, "preprocess: logits, bias and gates must be 4-byte aligned");
+    const Range rx[] = {{xq, NH * d * eb}, {xk, NH * d * eb}, {xv, NH * d * eb}, {conv_w, (size_t)12 * H * d * 4},
+                        {a_logit, NH * 4}, {b_logit, NH * 4}, {gate_bias, (size_t)H * 4},
+                        {cu_seqlens, cu_seqlens ? (size_t)(n_seq + 1) * 4 : 0}, {conv_state_in, sb}};
+    const Range ry[] = {{q, NH * d * eb}, {k, NH * d * eb}, {v, NH * d * eb}, {g, NH * 4}, {beta, NH * 4}};
+    const Range rso{conv_state_out, sb};
+    for (const Range &o : ry) {
+        for (const Range &i : rx)
+            if (overlap(o, i)) return fail(GDN_ERR_ALIAS, "preprocess: an output overlaps an input");
+        for (const Range &o2 : ry)
+            if (&o2 != &o && overlap(o, o2)) return fail(GDN_ERR_ALIAS, "preprocess: outputs overlap");
+        if (overlap(o, rso)) return fail(GDN_ERR_ALIAS, "preprocess: an output overlaps conv_state_out");
+    }
+    for (const Range &i : rx)
+        if (i.p != conv_state_in && overlap(rso, i)) return fail(GDN_ERR_ALIAS, "preprocess: conv_state_out overlaps an input");
+    if (conv_state_in && conv_state_in != conv_state_out && overlap(rso, Range{conv_state_in, sb}))
+        return fail(GDN_ERR_ALIAS, "preprocess: conv_state_in partially overlaps conv_state_out");
+    return hip_status(gdn::launch_preprocess(dtype == GDN_BF16, d, xq, xk, xv, conv_w, conv_state_in, conv_state_out,
+                                             a_logit, b_logit, gate_bias, cu_seqlens, n_seq, total_tokens, H,
+                                             activation, q, k, v, g, beta, (hipStream_t)stream),
+                      "preprocess launch");
+}
+
 }  // extern "C"

@@ -22,9 +22,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     return u >> 16;
 }
 
-// Two fp32 -> one dword of two bf16 (a in the low half).
+// Two fp32 -> one dword of two bf16 (a in the low half), rounded to nearest
+// even by the conversion instruction (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------------------

@@ -35,6 +35,13 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v,
                                   float *o, float *final_state, void *workspace,
                                   const hipEvent_t *marks, hipStream_t stream);
 
+// Pre-processing: conv (4 taps) + optional SiLU + L2 norm of q, k + gate maps,
+// then the returned conv state.
+hipError_t launch_preprocess(bool bf16, int d, const void *xq, const void *xk, const void *xv, const float *w,
+                             const void *st_in, void *st_out, const float *a_logit, const float *b_logit,
+                             const float *bias, const int32_t *cu, int64_t n_seq, int64_t total_tokens, int H, int act,
+                             void *q, void *k, void *v, float *g, float *beta, hipStream_t stream);
+
 // state[0 : n_floats] = init ? init : 0
 hipError_t launch_state_fill(float *state, const float *init, int64_t n_floats, hipStream_t stream);
 // zero blocks slots[i] (each block_floats long) for 0 <= slots[i] < n_blocks

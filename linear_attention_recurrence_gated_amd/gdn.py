@@ -8,6 +8,7 @@ Names mirror include/gdn.h:
     prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=0) -> (o, final_state)
     decode_step(q, k, v, g, beta, state) -> o          (state updated in place)
     state_init(state, init=None), state_reset(state, slots=None)
+    preprocess(xq, xk, xv, conv_w, a_logit, b_logit, ...) -> (q, k, v, g, beta, conv_state)
     prefill_set_marks([ev0, ev1, ev2])                 (profiling hook)
     state_bytes(...), prefill_workspace_bytes(...), prefill_algorithm(...)
 """
@@ -20,6 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdn.so")
 
 GDN_BF16, GDN_FP32 = 0, 1
+GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 CHUNK_AUTO, CHUNK_SERIAL, CHUNK_64 = 0, 1, 64
 
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
@@ -38,6 +40,8 @@ SIGNATURES = {
                            _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "gdn_decode_step": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "gdn_prefill_set_marks": (_i32, [ctypes.POINTER(_vp), _i32]),
+    "gdn_preprocess": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
+                              _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gdn_status_string": (ctypes.c_char_p, [_i32]),
     "gdn_last_error": (ctypes.c_char_p, []),
 }
@@ -208,3 +212,53 @@ def decode_step(q, k, v, g, beta, state, out=None, stream=None):
         _dev_ptr(state, "state", torch.float32), _dev_ptr(out, "out", torch.float32),
         B, H, dk, dv, _stream(k.device, stream)))
     return out
+
+
+def _cu_pair(cu_seqlens, cu_seqlens_device, dev):
+    import torch
+    if cu_seqlens is None:
+        return 1, None, None
+    cu_host = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if torch.is_tensor(cu_seqlens) else cu_seqlens,
+                                              dtype=np.int32))
+    cu_dev = cu_seqlens_device if cu_seqlens_device is not None else torch.from_numpy(cu_host).to(dev)
+    return cu_host.shape[0] - 1, cu_host, cu_dev
+
+
+def preprocess(xq, xk, xv, conv_w, a_logit, b_logit, gate_bias=None, cu_seqlens=None, conv_state_in=None,
+               conv_state_out=None, activation=GDN_ACT_NONE, cu_seqlens_device=None, out=None, stream=None):
+    """Convolution (4 taps, causal, depthwise), optional SiLU, L2 norm of q and
+    k, and the gate maps, in front of prefill() or decode_step().
+
+    xq, xk, xv: [N, H, d] (bf16 or fp32, device); conv_w: [3, H, d, 4] fp32;
+    a_logit, b_logit: [N, H] fp32; gate_bias: [H] fp32 or None.
+    conv_state_in / conv_state_out: [n_seq, 3, 3, H, d] in the dtype of xq
+    (None in: zeros; they may be the same tensor).  activation: GDN_ACT_NONE,
+    GDN_ACT_SILU or "none" / "silu".  out: optional (q, k, v, g, beta).
+    Returns (q, k, v, g, beta, conv_state_out).
+    """
+    import torch
+    N, H, d = xk.shape
+    dev = xk.device
+    if isinstance(activation, str):
+        activation = {"none": GDN_ACT_NONE, "silu": GDN_ACT_SILU}[activation]
+    n_seq, cu_host, cu_dev = _cu_pair(cu_seqlens, cu_seqlens_device, dev)
+    code = _dtype_code(xk)
+    for name, t in (("xq", xq), ("xv", xv)):
+        if t.dtype != xk.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from xk dtype {xk.dtype}")
+    if out is None:
+        out = (torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv),
+               torch.empty((N, H), dtype=torch.float32, device=dev), torch.empty((N, H), dtype=torch.float32, device=dev))
+    q, k, v, g, beta = out
+    if conv_state_out is None:
+        conv_state_out = torch.empty((n_seq, 3, 3, H, d), dtype=xk.dtype, device=dev)
+    cu_host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    _check(lib().gdn_preprocess(
+        _dev_ptr(xq, "xq"), _dev_ptr(xk, "xk"), _dev_ptr(xv, "xv"), code,
+        _dev_ptr(conv_w, "conv_w", torch.float32), _dev_ptr(conv_state_in, "conv_state_in", xk.dtype),
+        _dev_ptr(conv_state_out, "conv_state_out", xk.dtype), _dev_ptr(a_logit, "a_logit", torch.float32),
+        _dev_ptr(b_logit, "b_logit", torch.float32), _dev_ptr(gate_bias, "gate_bias", torch.float32),
+        _dev_ptr(cu_dev, "cu_seqlens_device", torch.int32), cu_host_ptr, n_seq, N, H, d, activation,
+        _dev_ptr(q, "q", xk.dtype), _dev_ptr(k, "k", xk.dtype), _dev_ptr(v, "v", xk.dtype),
+        _dev_ptr(g, "g", torch.float32), _dev_ptr(beta, "beta", torch.float32), _stream(dev, stream)))
+    return q, k, v, g, beta, conv_state_out

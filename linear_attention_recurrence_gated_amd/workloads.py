@@ -253,6 +253,50 @@ def config5(H=48, d=128):
 
 
 # ---------------------------------------------------------------------------
+# Inputs of the pre-processing (convolution, norm and gate maps) in front of
+# the recurrence.
+
+@dataclass
+class PreprocessInputs:
+    xq: np.ndarray                     # [N, H, d] float32 holding run-dtype values
+    xk: np.ndarray
+    xv: np.ndarray
+    w: np.ndarray                      # [3, H, d, 4] float32 conv taps
+    a_logit: np.ndarray                # [N, H] float32
+    b_logit: np.ndarray                # [N, H] float32
+    bias: Optional[np.ndarray]         # [H] float32 or None
+    cu_seqlens: Optional[np.ndarray]   # [n_seq + 1] int32, or None
+    state_in: Optional[np.ndarray]     # [n_seq, 3, 3, H, d] float32 run-dtype values, or None
+    dtype: str = "bf16"
+    activation: str = "none"
+
+    @property
+    def n_seq(self):
+        return 1 if self.cu_seqlens is None else len(self.cu_seqlens) - 1
+
+
+def make_preprocess(lengths, H, d, dtype="bf16", seed=SEED_BASE + 6, with_state=True, with_bias=True,
+                    activation="none", packed=None):
+    """Raw projections x ~ N(0, 1) rounded to the run dtype; conv taps uniform
+    in [-1/2, 1/2] (the default init bound 1/sqrt(fan_in) of a depthwise
+    kernel of 4 taps); logits a, b ~ N(0, 1); per-head bias uniform in [0, 4];
+    starting conv states ~ N(0, 1) rounded to the run dtype."""
+    lengths = [int(x) for x in lengths]
+    N, n = sum(lengths), len(lengths)
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    x = [_round_run_dtype(rng.standard_normal((N, H, d), dtype=np.float32), dtype) for _ in range(3)]
+    w = rng.uniform(-0.5, 0.5, size=(3, H, d, 4)).astype(np.float32)
+    a = rng.standard_normal((N, H), dtype=np.float32)
+    b = rng.standard_normal((N, H), dtype=np.float32)
+    bias = rng.uniform(0.0, 4.0, size=H).astype(np.float32) if with_bias else None
+    st = _round_run_dtype(rng.standard_normal((n, 3, 3, H, d), dtype=np.float32), dtype) if with_state else None
+    if packed is None:
+        packed = n != 1
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32) if packed else None
+    return PreprocessInputs(x[0], x[1], x[2], w, a, b, bias, cu, st, dtype, activation)
+
+
+# ---------------------------------------------------------------------------
 # Device placement (torch is used for memory only).
 
 def to_torch(x, dtype, device):

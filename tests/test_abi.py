@@ -170,3 +170,53 @@ def test_prefill_set_marks_validation():
     assert L.gdn_prefill_set_marks(None, 2) == 1
     assert L.gdn_prefill_set_marks(arr, 3) == 0  # all NULL: armed with nothing
     assert L.gdn_prefill_set_marks(None, 0) == 0
+
+
+def _preprocess(**kw):
+    # N=64 tokens, H=2, d=16 bf16: every tensor is 4 KiB, so the regions below are disjoint.
+    a = dict(xq=FAKE, xk=FAKE * 2, xv=FAKE * 3, dtype=gdn.GDN_BF16, w=FAKE * 4, sin=None, sout=FAKE * 5,
+             a=FAKE * 6, b=FAKE * 7, bias=None, cu=None, cu_host=None, n_seq=1, N=64, H=2, d=16, act=0,
+             q=FAKE * 8, k=FAKE * 9, v=FAKE * 10, g=FAKE * 11, beta=FAKE * 12)
+    a.update(kw)
+    L = gdn.lib()
+    st = L.gdn_preprocess(a["xq"], a["xk"], a["xv"], a["dtype"], a["w"], a["sin"], a["sout"], a["a"], a["b"],
+                          a["bias"], a["cu"], a["cu_host"], a["n_seq"], a["N"], a["H"], a["d"], a["act"], a["q"],
+                          a["k"], a["v"], a["g"], a["beta"], None)
+    return st, L.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(dtype=7), 3),
+    (dict(H=0), 2),
+    (dict(N=-3), 2),
+    (dict(d=48), 7),
+    (dict(act=2), 7),
+    (dict(sout=None), 1),
+    (dict(xk=None), 1),
+    (dict(beta=None), 1),
+    (dict(n_seq=2), 5),
+    (dict(xq=FAKE + 8), 4),
+    (dict(sin=FAKE * 13 + 4), 4),
+    (dict(g=FAKE * 11 + 2), 4),
+    (dict(q=FAKE), 8),                      # output q on top of input xq
+    (dict(g=FAKE * 6), 8),                  # gate on top of its logit
+    (dict(k=FAKE * 8), 8),                  # two outputs on one buffer
+    (dict(sout=FAKE * 9), 8),               # conv state on top of output k
+    (dict(sout=FAKE * 3), 8),               # conv state on top of input xv
+    (dict(sin=FAKE * 5 + 16), 8),           # starting state partly overlapping the returned one
+])
+def test_preprocess_validation(kw, code):
+    st, msg = _preprocess(**kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_preprocess_seqlens_validation():
+    for cu in (np.array([0, 30, 20, 64], np.int32), np.array([0, 30, 40, 60], np.int32)):
+        st, msg = _preprocess(cu=FAKE * 64, cu_host=_host(cu), n_seq=3)
+        assert st == 5, msg
+    st, _ = _preprocess(cu=FAKE * 64, cu_host=None, n_seq=3)
+    assert st == 1
+    empty = np.array([0], np.int32)
+    st, _ = _preprocess(cu=FAKE * 64, cu_host=_host(empty), n_seq=0, N=0)
+    assert st == 0  # nothing to do, nothing enqueued
