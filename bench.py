@@ -178,6 +178,49 @@ def bench_decode(torch, gdn, w, steps, rotate):
     return ms
 
 
+def bench_decode_slots(torch, gdn, w, steps, rotate):
+    """Serving form of the decode step: the 64 rows of the batch take a fixed
+    random permutation of 64 of the 128 slots of a state pool (one pool per
+    layer, `rotate` layers), with no host-side slot check.  Timed eagerly and
+    as replays of one captured HIP graph per pool; returns (eager, graph)."""
+    import numpy as np
+    dec = w.config3(steps=1, B=DEC_B, H=H, d=D)
+    dev = "cuda:0"
+    n_slots = 2 * DEC_B
+    q = w.to_torch(dec.q[0], "bf16", dev)
+    k = w.to_torch(dec.k[0], "bf16", dev)
+    v = w.to_torch(dec.v[0], "bf16", dev)
+    g = torch.from_numpy(dec.g[0]).to(dev)
+    beta = torch.from_numpy(dec.beta[0]).to(dev)
+    slots = torch.from_numpy(np.random.default_rng(7).permutation(n_slots)[:DEC_B].astype(np.int32)).to(dev)
+    pools = [torch.zeros((n_slots, H, D, D), dtype=torch.float32, device=dev) for _ in range(rotate)]
+    o = torch.empty((DEC_B, H, D), dtype=torch.float32, device=dev)
+
+    def step(pool):
+        gdn.decode_step_slots(q, k, v, g, beta, pool, slots, slots_host=None, out=o)
+
+    def timed(fns):
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for t, (a, b) in enumerate(ev):
+            a.record()
+            fns[t % len(fns)]()
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)
+
+    eager = timed([lambda p=p: step(p) for p in pools])
+    graphs = []
+    for pool in pools:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step(pool)
+        graphs.append(gr)
+    return eager, timed([gr.replay for gr in graphs])
+
+
 def bench_preprocess(torch, gdn, w, steps, warmup, rotate):
     """gdn_preprocess over the one-layer prefill shape (T = 4096, H = 48,
     d = 128, bf16, SiLU, with conv state and gate bias); successive calls cycle
@@ -282,7 +325,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of parts to time alone (prefill, decode, preprocess, copy), one JSON line each, for "
+                    help="comma list of parts to time alone (prefill, decode, decode_slots, preprocess, copy), one JSON line "
+                         "each, for "
                          "profiling runs; 'copy' is the byte-counter calibration copy")
     ap.add_argument("--warm", action="store_true",
                     help="also time one resident copy (inputs and state may then sit in the last-level cache)")
@@ -305,7 +349,7 @@ def main():
 
     if args.only:
         parts = args.only.split(",")
-        bad = [p for p in parts if p not in ("prefill", "decode", "preprocess", "copy")]
+        bad = [p for p in parts if p not in ("prefill", "decode", "decode_slots", "preprocess", "copy")]
         if bad:
             ap.error(f"--only: unknown part(s) {bad}")
         for part in parts:
@@ -316,6 +360,10 @@ def main():
             elif part == "decode":
                 dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
                 print(json.dumps({"only": "decode", "ms_per_step": mean(dec_ms)}), flush=True)
+            elif part == "decode_slots":
+                ds_ms, dg_ms = bench_decode_slots(torch, gdn, w, args.decode_steps, args.rotate)
+                print(json.dumps({"only": "decode_slots", "ms_per_step": mean(ds_ms),
+                                  "graph_replay_ms_per_step": mean(dg_ms)}), flush=True)
             elif part == "preprocess":
                 pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
                 print(json.dumps({"only": "preprocess", "ms_per_call": mean(pre_ms)}), flush=True)
@@ -325,6 +373,7 @@ def main():
     ms, ms_call, wall = bench_prefill(torch, gdn, w, args.steps, args.warmup, args.rotate)
     dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
     pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
+    ds_ms, dg_ms = bench_decode_slots(torch, gdn, w, args.decode_steps, args.rotate)
 
     step_ms = mean(ms)
     tok_s = T / (step_ms / 1e3)
@@ -388,6 +437,12 @@ def main():
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                                 "traffic": load_traffic("k_decode_step")}},
         "preprocess": pre_entry(pre_ms),
+        "decode_slots": {"ms_per_step": mean(ds_ms), "p50_ms": pct(ds_ms, 50), "p99_ms": pct(ds_ms, 99),
+                         "value": dec_bytes / (mean(ds_ms) / 1e3) / 1e9, "unit": "GB/s",
+                         "frac_hbm_peak": dec_bytes / (mean(ds_ms) / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "graph_replay_ms_per_step": mean(dg_ms),
+                         "workload": "config-3 step, 64 rows on a permutation of 64 of 128 pool slots; eager "
+                                     "launches, and replays of a captured HIP graph (event-bracketed)"},
         "rotate": args.rotate,
         "conditions": run_conditions(torch),
     }

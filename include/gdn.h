@@ -53,7 +53,8 @@ typedef enum {
     GDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than gdn_prefill_workspace_bytes() */
     GDN_ERR_UNSUPPORTED = 7, /* head dimension, dtype or chunk size not built */
     GDN_ERR_ALIAS = 8,       /* an output overlaps an input it must not overlap */
-    GDN_ERR_HIP = 9          /* the HIP runtime reported an error */
+    GDN_ERR_HIP = 9,         /* the HIP runtime reported an error */
+    GDN_ERR_SLOTS = 10       /* a state slot out of range, or one slot used twice in a batch */
 } gdn_status;
 
 /* Prefill algorithms (the `chunk` argument of gdn_prefill). */
@@ -133,6 +134,31 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtype dtype,
                            const float *g, const float *beta, float *state, float *o,
                            int64_t B, int32_t H, int32_t dk, int32_t dv, void *stream);
+
+/* One token for each of B requests whose states live in a pool of n_slots
+ * states, the serving form of gdn_decode_step.  "Hybrid · kết hợp nhiều cơ
+ * chế..." (openarchlab.com), section 3: a runtime needs state-update and
+ * batch/reset rules, and its memory planning must count the recurrent state
+ * (gdn_state_bytes(n_slots, ...) for the pool).  Row b of the batch reads and
+ * updates state slot slots[b] in place; slots are assigned by the caller, and a
+ * slot handed to a new request is cleared first with gdn_state_reset.
+ *
+ *   q, k, v, g, beta, o   as for gdn_decode_step, with B rows
+ *   state_pool   [n_slots][H][dv][dk] fp32, updated in place for the slots used
+ *   slots        device int32 [B]: the slot of each row; -1 marks a padding row,
+ *                whose o row is written as zeros and which touches no state
+ *   slots_host   optional host copy of slots, checked before anything is
+ *                enqueued: every entry in [-1, n_slots) and no slot twice
+ *                (GDN_ERR_SLOTS otherwise).  Pass NULL when the device array
+ *                changes after the call is recorded (a captured graph): the
+ *                kernel then treats any entry outside [0, n_slots) as padding,
+ *                and two rows naming one slot race, which the caller must avoid.
+ * Nothing here allocates or synchronises, so the call can be captured in a
+ * HIP graph together with gdn_state_reset. */
+gdn_status gdn_decode_step_slots(const void *q, const void *k, const void *v, gdn_dtype dtype,
+                                 const float *g, const float *beta, float *state_pool, int64_t n_slots,
+                                 const int32_t *slots, const int32_t *slots_host, float *o,
+                                 int64_t B, int32_t H, int32_t dk, int32_t dv, void *stream);
 
 /* Activation after the pre-processing convolution. */
 typedef enum { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_activation;

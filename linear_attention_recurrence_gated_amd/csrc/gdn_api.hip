@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <vector>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -114,6 +115,7 @@ const char *gdn_status_string(gdn_status s) {
         case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
         case GDN_ERR_ALIAS: return "overlapping buffers";
         case GDN_ERR_HIP: return "HIP runtime error";
+        case GDN_ERR_SLOTS: return "invalid state slots";
     }
     return "unknown status";
 }
@@ -267,9 +269,54 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtyp
         if (overlap(ro, in)) return fail(GDN_ERR_ALIAS, "decode_step: o overlaps another argument");
     for (Range in : {rq, rk, rv, rg, rb})
         if (overlap(rs, in)) return fail(GDN_ERR_ALIAS, "decode_step: state overlaps an input");
-    return hip_status(gdn::launch_decode(dtype == GDN_BF16, dk, q, k, v, g, beta, state, o, (int64_t)BH,
-                                         (hipStream_t)stream),
+    return hip_status(gdn::launch_decode(dtype == GDN_BF16, dk, q, k, v, g, beta, state, o, (int64_t)BH, H, nullptr,
+                                         0, (hipStream_t)stream),
                       "decode_step launch");
+}
+
+gdn_status gdn_decode_step_slots(const void *q, const void *k, const void *v, gdn_dtype dtype, const float *g,
+                                 const float *beta, float *state_pool, int64_t n_slots, const int32_t *slots,
+                                 const int32_t *slots_host, float *o, int64_t B, int32_t H, int32_t dk, int32_t dv,
+                                 void *stream) {
+    if (dtype != GDN_BF16 && dtype != GDN_FP32)
+        return fail(GDN_ERR_DTYPE, "decode_step_slots: dtype %d", (int)dtype);
+    if (B < 0 || H <= 0 || n_slots < 0 || B * (int64_t)H > (int64_t)UINT32_MAX || n_slots > (int64_t)INT32_MAX)
+        return fail(GDN_ERR_SHAPE, "decode_step_slots: B=%lld H=%d n_slots=%lld", (long long)B, H,
+                    (long long)n_slots);
+    if (!supported_d(dk, dv))
+        return fail(GDN_ERR_UNSUPPORTED, "decode_step_slots: dk=%d dv=%d not supported", dk, dv);
+    if (B == 0) return ok();
+    if (!q || !k || !v || !g || !beta || !o || !slots)
+        return fail(GDN_ERR_NULL, "decode_step_slots: q, k, v, g, beta, slots and o are required");
+    if (n_slots > 0 && !state_pool) return fail(GDN_ERR_NULL, "decode_step_slots: state_pool is NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state_pool, 16) || !aligned(o, 16))
+        return fail(GDN_ERR_ALIGN, "decode_step_slots: q, k, v, state_pool and o must be 16-byte aligned");
+    if (!aligned(g, 4) || !aligned(beta, 4) || !aligned(slots, 4))
+        return fail(GDN_ERR_ALIGN, "decode_step_slots: g, beta and slots must be 4-byte aligned");
+    if (slots_host) {
+        std::vector<uint8_t> used((size_t)n_slots, 0);
+        for (int64_t b = 0; b < B; ++b) {
+            const int32_t sl = slots_host[b];
+            if (sl < -1 || sl >= n_slots)
+                return fail(GDN_ERR_SLOTS, "decode_step_slots: slots[%lld] = %d outside [-1, %lld)", (long long)b,
+                            sl, (long long)n_slots);
+            if (sl >= 0) {
+                if (used[(size_t)sl])
+                    return fail(GDN_ERR_SLOTS, "decode_step_slots: slot %d appears twice in the batch", sl);
+                used[(size_t)sl] = 1;
+            }
+        }
+    }
+    const size_t eb = elem_bytes(dtype), BH = (size_t)B * H;
+    const Range rq{q, BH * dk * eb}, rk{k, BH * dk * eb}, rv{v, BH * dv * eb}, rg{g, BH * 4}, rb{beta, BH * 4},
+        rsl{slots, (size_t)B * 4}, rs{state_pool, gdn_state_bytes(n_slots, H, dk, dv)}, ro{o, BH * dv * 4};
+    for (Range in : {rq, rk, rv, rg, rb, rsl, rs})
+        if (overlap(ro, in)) return fail(GDN_ERR_ALIAS, "decode_step_slots: o overlaps another argument");
+    for (Range in : {rq, rk, rv, rg, rb, rsl})
+        if (overlap(rs, in)) return fail(GDN_ERR_ALIAS, "decode_step_slots: state_pool overlaps an input");
+    return hip_status(gdn::launch_decode(dtype == GDN_BF16, dk, q, k, v, g, beta, state_pool, o, (int64_t)BH, H,
+                                         slots, n_slots, (hipStream_t)stream),
+                      "decode_step_slots launch");
 }
 
 gdn_status gdn_preprocess(const void *xq, const void *xk, const void *xv, gdn_dtype dtype, const float *conv_w,

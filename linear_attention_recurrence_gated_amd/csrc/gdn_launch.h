@@ -10,9 +10,9 @@
 namespace gdn {
 
 // One decode step for B*H heads (in-place state update).
-hipError_t launch_decode(bool bf16, int d, const void *q, const void *k, const void *v,
-                         const float *g, const float *beta, float *state, float *o,
-                         int64_t BH, hipStream_t stream);
+hipError_t launch_decode(bool bf16, int d, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, float *state, float *o, int64_t BH, int H, const int32_t *slots,
+                         int64_t n_slots, hipStream_t stream);
 
 // marks[3]: events (or nullptr) recorded on `stream` before the first kernel,
 // after the state-independent kernels and after the state chain.

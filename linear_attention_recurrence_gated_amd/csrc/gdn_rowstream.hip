@@ -34,11 +34,15 @@ struct RowLayout {
 // ---------------------------------------------------------------------------
 // Decode: grid = B*H workgroups of NW waves; wave w owns rows [w*D/NW, (w+1)*D/NW).
 // NT: stream the state with non-temporal loads and stores (large batches).
+// slots: NULL for state [B][H][dv][dk]; else row b of the batch uses state
+// slot slots[b] of a pool [n_slots][H][dv][dk], and a row whose slot lies
+// outside [0, n_slots) is padding: its o row is zeroed, no state is touched.
 template <typename TIn, int D, int NW, bool NT>
 __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                          const TIn *__restrict__ v, const float *__restrict__ g,
                                                          const float *__restrict__ beta, float *__restrict__ state,
-                                                         float *__restrict__ o) {
+                                                         float *__restrict__ o, const int32_t *__restrict__ slots,
+                                                         int64_t n_slots, int H) {
     using L = RowLayout<D>;
     constexpr int RPW = D / NW;
     constexpr int PASSES = (RPW + L::RPP - 1) / L::RPP;
@@ -46,13 +50,23 @@ __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane % L::LPR, rs = lane / L::LPR;
     const int c0 = 4 * lr, c1 = D / 2 + 4 * lr;
+    int64_t sh = bh;  // (state slot, head) index
+    if (slots) {
+        const int64_t b = bh / H;
+        const int32_t slot = slots[b];
+        if (slot < 0 || slot >= n_slots) {  // padding row (uniform across the workgroup)
+            for (int i = threadIdx.x; i < D; i += 64 * NW) o[bh * D + i] = 0.f;
+            return;
+        }
+        sh = (int64_t)slot * H + (bh - b * H);
+    }
 
     const TIn *kp = k + bh * D;
     const TIn *qp = q + bh * D;
     const float4 k0 = In<TIn>::load4(kp + c0), k1 = In<TIn>::load4(kp + c1);
     const float4 q0 = In<TIn>::load4(qp + c0), q1 = In<TIn>::load4(qp + c1);
     const float gt = g[bh], bt = beta[bh];
-    float *S = state + bh * (int64_t)D * D;
+    float *S = state + sh * (int64_t)D * D;
 
     float4 s0[PASSES], s1[PASSES];
     float vr[PASSES];
@@ -180,24 +194,26 @@ constexpr int64_t DECODE_NT_MIN_BYTES = int64_t(32) << 20;
 
 template <typename TIn, int D>
 static hipError_t decode_d(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                           float *state, float *o, int64_t BH, hipStream_t stream) {
+                           float *state, float *o, int64_t BH, int H, const int32_t *slots, int64_t n_slots,
+                           hipStream_t stream) {
     constexpr int NW = D >= 64 ? 4 : 1;
     if (BH * D * D * 4 >= DECODE_NT_MIN_BYTES)
         hipLaunchKernelGGL((k_decode_step<TIn, D, NW, true>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
-                           (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o);
+                           (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o, slots, n_slots, H);
     else
         hipLaunchKernelGGL((k_decode_step<TIn, D, NW, false>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
-                           (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o);
+                           (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o, slots, n_slots, H);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(bool bf16, int d, const void *q, const void *k, const void *v, const float *g,
-                         const float *beta, float *state, float *o, int64_t BH, hipStream_t stream) {
+                         const float *beta, float *state, float *o, int64_t BH, int H, const int32_t *slots,
+                         int64_t n_slots, hipStream_t stream) {
     if (BH == 0) return hipSuccess;
-#define GDN_DEC(D)                                                                          \
-    case D:                                                                                 \
-        return bf16 ? decode_d<uint16_t, D>(q, k, v, g, beta, state, o, BH, stream)         \
-                    : decode_d<float, D>(q, k, v, g, beta, state, o, BH, stream);
+#define GDN_DEC(D)                                                                                      \
+    case D:                                                                                             \
+        return bf16 ? decode_d<uint16_t, D>(q, k, v, g, beta, state, o, BH, H, slots, n_slots, stream) \
+                    : decode_d<float, D>(q, k, v, g, beta, state, o, BH, H, slots, n_slots, stream);
     switch (d) {
         GDN_DEC(16)
         GDN_DEC(32)

@@ -7,6 +7,7 @@ missing or fails to load, every call raises.
 Names mirror include/gdn.h:
     prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=0) -> (o, final_state)
     decode_step(q, k, v, g, beta, state) -> o          (state updated in place)
+    decode_step_slots(q, k, v, g, beta, pool, slots) -> o   (slot b of the pool per row)
     state_init(state, init=None), state_reset(state, slots=None)
     preprocess(xq, xk, xv, conv_w, a_logit, b_logit, ...) -> (q, k, v, g, beta, conv_state)
     prefill_set_marks([ev0, ev1, ev2])                 (profiling hook)
@@ -26,7 +27,7 @@ CHUNK_AUTO, CHUNK_SERIAL, CHUNK_64 = 0, 1, 64
 
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_SEQLENS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_UNSUPPORTED", 8: "GDN_ERR_ALIAS",
-          9: "GDN_ERR_HIP"}
+          9: "GDN_ERR_HIP", 10: "GDN_ERR_SLOTS"}
 
 # Every symbol include/gdn.h declares, with (restype, argtypes).
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -39,6 +40,8 @@ SIGNATURES = {
     "gdn_prefill": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32,
                            _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "gdn_decode_step": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "gdn_decode_step_slots": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i32, _i32,
+                                     _i32, _vp]),
     "gdn_prefill_set_marks": (_i32, [ctypes.POINTER(_vp), _i32]),
     "gdn_preprocess": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
                               _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -262,3 +265,31 @@ def preprocess(xq, xk, xv, conv_w, a_logit, b_logit, gate_bias=None, cu_seqlens=
         _dev_ptr(q, "q", xk.dtype), _dev_ptr(k, "k", xk.dtype), _dev_ptr(v, "v", xk.dtype),
         _dev_ptr(g, "g", torch.float32), _dev_ptr(beta, "beta", torch.float32), _stream(dev, stream)))
     return q, k, v, g, beta, conv_state_out
+
+
+def decode_step_slots(q, k, v, g, beta, state_pool, slots, slots_host="auto", out=None, stream=None):
+    """One token for each of B requests; row b updates state_pool[slots[b]]
+    ([n_slots, H, dv, dk] fp32) in place; slots[b] = -1 marks a padding row
+    (o row zeroed).  slots: device int32 [B].  slots_host: "auto" copies slots
+    to the host for validation (a synchronising copy), None skips it (for graph
+    capture), or a host array given by the caller.  Returns o [B, H, dv] fp32."""
+    import torch
+    B, H, dk = k.shape
+    dv = v.shape[2]
+    n_slots = state_pool.shape[0]
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=torch.float32, device=k.device)
+    if isinstance(slots_host, str):
+        slots_host = slots.cpu().numpy()
+    host = None
+    if slots_host is not None:
+        host = np.ascontiguousarray(np.asarray(slots_host, dtype=np.int32))
+        if host.shape != (B,):
+            raise ValueError(f"slots_host must have shape ({B},)")
+    _check(lib().gdn_decode_step_slots(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k),
+        _dev_ptr(g, "g", torch.float32), _dev_ptr(beta, "beta", torch.float32),
+        _dev_ptr(state_pool, "state_pool", torch.float32), n_slots, _dev_ptr(slots, "slots", torch.int32),
+        None if host is None else host.ctypes.data_as(ctypes.c_void_p),
+        _dev_ptr(out, "out", torch.float32), B, H, dk, dv, _stream(k.device, stream)))
+    return out

@@ -220,3 +220,42 @@ def test_preprocess_seqlens_validation():
     empty = np.array([0], np.int32)
     st, _ = _preprocess(cu=FAKE * 64, cu_host=_host(empty), n_seq=0, N=0)
     assert st == 0  # nothing to do, nothing enqueued
+
+
+def _decode_slots(**kw):
+    # B = 4 rows, H = 2, d = 16, bf16: q, k, v 256 B each; the pool is 8 slots x 2 KiB
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, dtype=gdn.GDN_BF16, g=FAKE * 4, beta=FAKE * 5, pool=FAKE * 64,
+             n_slots=8, slots=FAKE * 6, slots_host=None, o=FAKE * 7, B=4, H=2, dk=16, dv=16)
+    a.update(kw)
+    L = gdn.lib()
+    st = L.gdn_decode_step_slots(a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"], a["pool"], a["n_slots"],
+                                 a["slots"], a["slots_host"], a["o"], a["B"], a["H"], a["dk"], a["dv"], None)
+    return st, L.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(dtype=4), 3),
+    (dict(B=-1), 2),
+    (dict(n_slots=-2), 2),
+    (dict(dk=16, dv=32), 7),
+    (dict(slots=None), 1),
+    (dict(pool=None), 1),
+    (dict(slots=FAKE * 6 + 2), 4),
+    (dict(o=FAKE * 7 + 8), 4),
+    (dict(o=FAKE * 6), 8),                   # o on top of slots
+    (dict(pool=FAKE * 2), 8),                # pool on top of k
+])
+def test_decode_slots_validation(kw, code):
+    st, msg = _decode_slots(**kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_decode_slots_host_checks():
+    for bad in ([0, 8, 1, 2], [0, -2, 1, 2], [3, 1, 3, -1]):   # out of range, below -1, a slot twice
+        host = np.array(bad, np.int32)
+        st, msg = _decode_slots(slots_host=_host(host))
+        assert st == 10, msg
+        assert gdn.lib().gdn_status_string(10).decode() == "invalid state slots"
+    st, _ = _decode_slots(B=0)
+    assert st == 0  # nothing to do, nothing enqueued
