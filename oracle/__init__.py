@@ -37,6 +37,8 @@ def load(path=LIB_PATH):
     lib.gdn_oracle_run.argtypes = [dp, dp, dp, dp, dp, ip, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    dp, dp, dp, ctypes.c_int]
+    lib.gdn_oracle_run_variant.restype = ctypes.c_int
+    lib.gdn_oracle_run_variant.argtypes = lib.gdn_oracle_run.argtypes + [ctypes.c_int]
     _libs[path] = lib
     return lib
 
@@ -58,19 +60,25 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def run(q, k, v, g, beta, cu_seqlens=None, s_init=None, threads=None, lib_path=LIB_PATH):
+NO_GATE, NO_ERASE = 1, 2
+
+
+def run(q, k, v, g, beta, cu_seqlens=None, s_init=None, threads=None, lib_path=LIB_PATH, variant=0):
     """Run the recurrence over a packed batch.
 
     q, k: [N, H, dk]; v: [N, H, dv]; g, beta: [N, H]; any real dtype (converted
     exactly to float64).  cu_seqlens: [n_seq + 1] integer offsets, or None for a
     single sequence.  s_init: [n_seq, H, dv, dk] or None (zeros).
+    variant: 0 (gated delta rule), or NO_GATE (g ignored; may be None) and/or
+    NO_ERASE (no recall term: the linear-attention write).
     Returns (o [N, H, dv], s_final [n_seq, H, dv, dk]) as float64.
     """
-    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    q, k, v, beta = (_f64(x) for x in (q, k, v, beta))
+    g = None if (g is None and variant & NO_GATE) else _f64(g)
     N, H, dk = k.shape
     dv = v.shape[2]
     assert q.shape == (N, H, dk) and v.shape[:2] == (N, H), "q/k/v shapes disagree"
-    assert g.shape == (N, H) and beta.shape == (N, H), "g/beta must be [N, H]"
+    assert (g is None or g.shape == (N, H)) and beta.shape == (N, H), "g/beta must be [N, H]"
     if cu_seqlens is None:
         cu = None
         n_seq = 1
@@ -84,15 +92,15 @@ def run(q, k, v, g, beta, cu_seqlens=None, s_init=None, threads=None, lib_path=L
     s_final = np.zeros((n_seq, H, dv, dk), dtype=np.float64)
     lib = load(lib_path)
     cu_ptr = None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
-    rc = lib.gdn_oracle_run(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu_ptr,
-                            n_seq, N, H, dk, dv, _ptr(s0), _ptr(o), _ptr(s_final),
-                            int(threads or default_threads()))
+    rc = lib.gdn_oracle_run_variant(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu_ptr,
+                                    n_seq, N, H, dk, dv, _ptr(s0), _ptr(o), _ptr(s_final),
+                                    int(threads or default_threads()), int(variant))
     if rc != 0:
         raise ValueError(f"gdn_oracle_run rejected its arguments (code {rc})")
     return o, s_final
 
 
-def run_decode(q, k, v, g, beta, s_init, threads=None, lib_path=LIB_PATH):
+def run_decode(q, k, v, g, beta, s_init, threads=None, lib_path=LIB_PATH, variant=0):
     """Oracle for repeated single-token steps on a batch of states.
 
     q, k: [steps, B, H, dk]; v: [steps, B, H, dv]; g, beta: [steps, B, H];
@@ -101,12 +109,13 @@ def run_decode(q, k, v, g, beta, s_init, threads=None, lib_path=LIB_PATH):
     contiguous.  Returns (o [steps, B, H, dv], s_final [B, H, dv, dk]).
     """
     q, k, v = (np.asarray(x) for x in (q, k, v))
-    g, beta = np.asarray(g), np.asarray(beta)
+    beta = np.asarray(beta)
+    g = beta if (g is None and variant & NO_GATE) else np.asarray(g)  # ignored then
     steps, B, H, dk = k.shape
     dv = v.shape[3]
     pack = lambda x: np.ascontiguousarray(np.swapaxes(x, 0, 1)).reshape((B * steps,) + x.shape[2:])
     cu = np.arange(B + 1, dtype=np.int64) * steps
-    o, s = run(pack(q), pack(k), pack(v), pack(g), pack(beta), cu, s_init, threads, lib_path)
+    o, s = run(pack(q), pack(k), pack(v), pack(g), pack(beta), cu, s_init, threads, lib_path, variant)
     o = np.swapaxes(o.reshape(B, steps, H, dv), 0, 1)
     return o, s
 

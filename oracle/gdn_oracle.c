@@ -36,6 +36,13 @@
  *     initial state (zeros when none is given).  A sequence of length zero
  *     returns its initial state unchanged.
  *
+ *   Variants (gdn_oracle_run_variant), from the same section's equations:
+ *   - bit 1, no gate: g_t = 1, the plain delta rule S_t = S_{t-1} +
+ *     beta_t (v_t - S_{t-1} k_t) k_t^T (g is ignored and may be NULL);
+ *   - bit 2, no erase: the recall term is dropped, S_t = g_t S_{t-1} +
+ *     beta_t v_t k_t^T, the linear-attention write (with both bits and
+ *     beta = 1: S_t = S_{t-1} + v_t k_t^T, plain linear attention).
+ *
  * Arithmetic: plain loops, j ascending, no fused multiply-add contraction
  * (built with -O2 -fno-fast-math -ffp-contract=off).  Because each token's
  * arithmetic depends only on the state and that token, splitting a sequence
@@ -59,6 +66,7 @@ typedef struct {
     const int64_t *cu;
     double *o, *s_final;
     int64_t n_seq, H, dk, dv;
+    int variant;       /* bit 1: no gate; bit 2: no erase term */
     int64_t next_unit; /* shared work counter, advanced atomically */
 } gdn_oracle_job;
 
@@ -78,13 +86,15 @@ static void run_unit(const gdn_oracle_job *J, int64_t unit, double *r) {
         const double *kt = J->k + (t * H + h) * dk;
         const double *qt = J->q + (t * H + h) * dk;
         const double *vt = J->v + (t * H + h) * dv;
-        const double gt = J->g[t * H + h];
+        const double gt = (J->variant & 1) ? 1.0 : J->g[t * H + h];
         const double bt = J->beta[t * H + h];
         double *ot = J->o + (t * H + h) * dv;
-        /* recall from the ungated previous state */
+        /* recall from the ungated previous state (nothing is erased without
+           the erase term) */
         for (int64_t i = 0; i < dv; ++i) {
             double acc = 0.0;
-            for (int64_t j = 0; j < dk; ++j) acc += S[i * dk + j] * kt[j];
+            if (!(J->variant & 2))
+                for (int64_t j = 0; j < dk; ++j) acc += S[i * dk + j] * kt[j];
             r[i] = acc;
         }
         /* gate the old state, then write the correction along the key */
@@ -117,14 +127,14 @@ static void *worker(void *arg) {
 
 /* Returns 0 on success, a negative code on invalid arguments (nothing is
  * written then), or -100 when a thread or buffer could not be created. */
-int gdn_oracle_run(const double *q, const double *k, const double *v,
-                   const double *g, const double *beta,
-                   const int64_t *cu_seqlens, int64_t n_seq, int64_t total_tokens,
-                   int64_t H, int64_t dk, int64_t dv,
-                   const double *s_init, double *o, double *s_final, int n_threads) {
-    if (n_seq < 0 || total_tokens < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+int gdn_oracle_run_variant(const double *q, const double *k, const double *v,
+                           const double *g, const double *beta,
+                           const int64_t *cu_seqlens, int64_t n_seq, int64_t total_tokens,
+                           int64_t H, int64_t dk, int64_t dv,
+                           const double *s_init, double *o, double *s_final, int n_threads, int variant) {
+    if (n_seq < 0 || total_tokens < 0 || H <= 0 || dk <= 0 || dv <= 0 || (variant & ~3)) return -1;
     if (!s_final) return -2;
-    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return -2;
+    if (total_tokens > 0 && (!q || !k || !v || (!g && !(variant & 1)) || !beta || !o)) return -2;
     if (!cu_seqlens) {
         if (n_seq != 1) return -3;
     } else {
@@ -138,6 +148,7 @@ int gdn_oracle_run(const double *q, const double *k, const double *v,
     J.cu = cu_seqlens ? cu_seqlens : one_seq;
     J.o = o; J.s_final = s_final;
     J.n_seq = n_seq; J.H = H; J.dk = dk; J.dv = dv;
+    J.variant = variant;
     J.next_unit = 0;
     if (n_seq == 0) return 0;
 
@@ -158,4 +169,14 @@ int gdn_oracle_run(const double *q, const double *k, const double *v,
     }
     free(tid);
     return failed ? -100 : 0;
+}
+
+/* The gated delta rule itself (variant 0). */
+int gdn_oracle_run(const double *q, const double *k, const double *v,
+                   const double *g, const double *beta,
+                   const int64_t *cu_seqlens, int64_t n_seq, int64_t total_tokens,
+                   int64_t H, int64_t dk, int64_t dv,
+                   const double *s_init, double *o, double *s_final, int n_threads) {
+    return gdn_oracle_run_variant(q, k, v, g, beta, cu_seqlens, n_seq, total_tokens, H, dk, dv, s_init, o, s_final,
+                                  n_threads, 0);
 }

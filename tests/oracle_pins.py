@@ -288,6 +288,75 @@ def pin_stability_bound(run):
             assert lhs <= rhs * (1 + 1e-12), f"norm bound broken at t={t}: {lhs} > {rhs}"
 
 
+# ---------------------------------------------------------------------------
+# Variants ([GDN] section 三: the linear-attention memory, the delta rule and
+# its gated form).  NO_GATE = 1 (g_t = 1), NO_ERASE = 2 (no recall term).
+
+NO_GATE, NO_ERASE = 1, 2
+
+
+def pin_variant_plain_linear_attention(run):
+    """No gate and no erase term, beta = 1: the linear-attention memory
+    S_t = S_0 + sum_{i<=t} v_i k_i^T and o_t = S_t q_t ([GDN], linear-attention
+    formulas), whatever g holds; unnormalised, non-orthogonal keys."""
+    T, H, dk, dv = 9, 2, 5, 4
+    q, k, v, g, _ = _inputs(81, T, H, dk, dv, unit_keys=False)
+    beta = np.ones((T, H))
+    s0 = _rng(82).standard_normal((1, H, dv, dk))
+    o, s = run(q, k, v, g, beta, None, s0, variant=NO_GATE | NO_ERASE)
+    for h in range(H):
+        mem = s0[0, h] + np.cumsum(np.einsum("ti,tj->tij", v[:, h], k[:, h]), axis=0)
+        _close(s[0, h], mem[-1], what="linear-attention memory")
+        _close(o[:, h], np.einsum("tij,tj->ti", mem, q[:, h]), what="linear-attention read-out")
+
+
+def pin_variant_gated_linear_attention(run):
+    """No erase term: S_t = (prod_{s<=t} g_s) S_0 + sum_{i<=t} (prod_{i<s<=t} g_s)
+    beta_i v_i k_i^T, written as an explicit sum of decayed writes."""
+    T, H, dk, dv = 8, 2, 4, 3
+    q, k, v, g, beta = _inputs(83, T, H, dk, dv, unit_keys=False, strength=(-0.5, 1.5))
+    s0 = _rng(84).standard_normal((1, H, dv, dk))
+    o, s = run(q, k, v, g, beta, None, s0, variant=NO_ERASE)
+    for h in range(H):
+        for t in range(T):
+            St = np.prod(g[:t + 1, h]) * s0[0, h]
+            for i in range(t + 1):
+                St = St + np.prod(g[i + 1:t + 1, h]) * beta[i, h] * np.outer(v[i, h], k[i, h])
+            _close(o[t, h], St @ q[t, h], what=f"decayed linear attention t={t}")
+        _close(s[0, h], St, what="decayed linear-attention memory")
+
+
+def pin_variant_delta_rule(run):
+    """No gate: the delta rule, equal to the explicit history expansion with
+    transitions A_s = I - beta_s k_s k_s^T; the g passed in is ignored."""
+    for seed, (T, dk, dv) in enumerate([(7, 4, 3), (5, 5, 5)]):
+        q, k, v, g, beta = _inputs(85 + seed, T, 1, dk, dv, unit_keys=False, strength=(-0.5, 1.5))
+        s0 = _rng(87 + seed).standard_normal((1, 1, dv, dk))
+        o, s = run(q, k, v, g, beta, None, s0, variant=NO_GATE)
+        o_ref, s_ref = _expand(q[:, 0], k[:, 0], v[:, 0], np.ones(T), beta[:, 0], s0[0, 0])
+        _close(o[:, 0], o_ref, tol=1e-11, what=f"delta-rule read-out {T}x{dk}x{dv}")
+        _close(s[0, 0], s_ref, tol=1e-11, what=f"delta-rule final state {T}x{dk}x{dv}")
+
+
+def pin_variant_delta_rule_repeated_key(run):
+    """No gate, one unit key written again and again: the recall along that key
+    is an exponential moving average, r_t = (1 - beta_t) r_{t-1} + beta_t v_t
+    (the delta rule as an online regression step, [GDN])."""
+    T, dk, dv = 12, 6, 3
+    r = _rng(89)
+    key = _unit(r.standard_normal(dk))
+    k = np.broadcast_to(key, (T, 1, dk)).copy()
+    q = k.copy()
+    v = r.standard_normal((T, 1, dv))
+    beta = r.uniform(0.0, 1.0, (T, 1))
+    g = r.uniform(0.2, 0.9, (T, 1))
+    o, _ = run(q, k, v, g, beta, variant=NO_GATE)
+    rt = np.zeros(dv)
+    for t in range(T):
+        rt = (1.0 - beta[t, 0]) * rt + beta[t, 0] * v[t, 0]
+        _close(o[t, 0], rt, what=f"moving average t={t}")
+
+
 ALL_PINS = [
     pin_per_token_closed_form,
     pin_unit_write,
@@ -300,4 +369,8 @@ ALL_PINS = [
     pin_segmented_equals_one_shot,
     pin_packed_sequences_are_independent,
     pin_stability_bound,
+    pin_variant_plain_linear_attention,
+    pin_variant_gated_linear_attention,
+    pin_variant_delta_rule,
+    pin_variant_delta_rule_repeated_key,
 ]

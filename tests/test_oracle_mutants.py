@@ -44,6 +44,12 @@ MUTANTS = {
     # state not reset between sequences of one head (carried from the previous one)
     "no_reset": ("memset(S, 0, (size_t)(dv * dk) * sizeof(double));",
                  "if (s > 0) memcpy(S, J->s_final + ((s - 1) * H + h) * dv * dk, (size_t)(dv * dk) * sizeof(double)); else memset(S, 0, (size_t)(dv * dk) * sizeof(double));"),
+    # variants: the no-erase flag ignored (recall still subtracted)
+    "variant_erase_kept": ("if (!(J->variant & 2))", "if (1)"),
+    # variants: the no-gate flag ignored (g still applied)
+    "variant_gate_kept": ("(J->variant & 1) ? 1.0 : J->g[t * H + h]", "J->g[t * H + h]"),
+    # variants: the two flags swapped
+    "variant_flags_swapped": ("if (!(J->variant & 2))", "if (!(J->variant & 1))"),
 }
 
 RUNNER = r"""
