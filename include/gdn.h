@@ -62,6 +62,21 @@ typedef enum {
 #define GDN_CHUNK_SERIAL 1   /* token-serial: one fixed-size update per token */
 #define GDN_CHUNK_64 64      /* chunkwise-parallel, 64-token chunks, MFMA (bf16 q/k/v, d = 128) */
 
+/* Variants of the recurrence (the `variant` argument of gdn_prefill,
+ * gdn_decode_step and gdn_decode_step_slots), from the equations of the
+ * Gated DeltaNet section (三) of "Qwen3.8-27B 架构深读":
+ *   GDN_VARIANT_GATED_DELTA  the gated delta rule above
+ *   GDN_VARIANT_NO_GATE      g = 1: the delta rule S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T;
+ *                            g is ignored and may be NULL
+ *   GDN_VARIANT_NO_ERASE     no recall term: S_t = g_t S_{t-1} + beta_t v_t k_t^T, the
+ *                            linear-attention write (with both flags and beta = 1:
+ *                            plain linear attention, S_t = S_{t-1} + v_t k_t^T)
+ * Flags may be combined; any other bit is GDN_ERR_UNSUPPORTED. */
+#define GDN_VARIANT_GATED_DELTA 0
+#define GDN_VARIANT_NO_GATE 1
+#define GDN_VARIANT_NO_ERASE 2
+#define GDN_VARIANT_MASK 3
+
 /* Bytes of fp32 state for n_seq sequences: n_seq * H * dv * dk * 4.
  * Returns 0 if a size is negative or zero (n_seq == 0 gives 0 as well).
  * The state is [n_seq][H][dv][dk]: row i of a head's state (its d_k entries)
@@ -96,7 +111,8 @@ size_t gdn_prefill_workspace_bytes(int64_t total_tokens, int64_t n_seq, int32_t 
  *
  *   q, k          [N][H][dk]  dtype, token-major, contiguous, 16-byte aligned
  *   v             [N][H][dv]  dtype
- *   g, beta       [N][H]      fp32 (gate and write strength per token and head)
+ *   g, beta       [N][H]      fp32 (gate and write strength per token and head);
+ *                             g is ignored, and may be NULL, with GDN_VARIANT_NO_GATE
  *   cu_seqlens    [n_seq+1]   int32 device copy of the sequence offsets, and
  *   cu_seqlens_host           the same offsets in host memory (validated here);
  *                             both NULL means one sequence (n_seq must be 1)
@@ -108,6 +124,7 @@ size_t gdn_prefill_workspace_bytes(int64_t total_tokens, int64_t n_seq, int32_t 
  *   chunk         GDN_CHUNK_AUTO, GDN_CHUNK_SERIAL or GDN_CHUNK_64
  *   workspace     device scratch of at least gdn_prefill_workspace_bytes();
  *                 may be NULL when that is 0.  Its contents on entry do not matter.
+ *   variant       GDN_VARIANT_* flags (0: the gated delta rule)
  *
  * Each sequence starts from its own initial state and never sees another
  * sequence's tokens; a zero-length sequence copies its initial state to its
@@ -120,20 +137,22 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
                        const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
                        int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
                        const float *initial_state, float *o, float *final_state,
-                       int32_t chunk, void *workspace, size_t workspace_bytes, void *stream);
+                       int32_t chunk, void *workspace, size_t workspace_bytes, int32_t variant,
+                       void *stream);
 
 /* One token for each of B sequences, updating their states in place.
  *
  *   q, k    [B][H][dk] dtype;   v [B][H][dv] dtype;   g, beta [B][H] fp32
  *   state   [B][H][dv][dk] fp32, read once and written once (in place)
  *   o       [B][H][dv] fp32, o = S_t q_t from the updated state
+ *   variant GDN_VARIANT_* flags (0: the gated delta rule)
  *
  * The per-token cost is fixed, whatever the position of the token ("Layouts
  * híbridos: três DeltaNet, uma attention" (llmdeepdive.com), section Conceito:
  * the state is a fixed set of matrices edited in place). */
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtype dtype,
                            const float *g, const float *beta, float *state, float *o,
-                           int64_t B, int32_t H, int32_t dk, int32_t dv, void *stream);
+                           int64_t B, int32_t H, int32_t dk, int32_t dv, int32_t variant, void *stream);
 
 /* One token for each of B requests whose states live in a pool of n_slots
  * states, the serving form of gdn_decode_step.  "Hybrid · kết hợp nhiều cơ
@@ -143,7 +162,7 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtyp
  * updates state slot slots[b] in place; slots are assigned by the caller, and a
  * slot handed to a new request is cleared first with gdn_state_reset.
  *
- *   q, k, v, g, beta, o   as for gdn_decode_step, with B rows
+ *   q, k, v, g, beta, o, variant   as for gdn_decode_step, with B rows
  *   state_pool   [n_slots][H][dv][dk] fp32, updated in place for the slots used
  *   slots        device int32 [B]: the slot of each row; -1 marks a padding row,
  *                whose o row is written as zeros and which touches no state
@@ -158,7 +177,7 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtyp
 gdn_status gdn_decode_step_slots(const void *q, const void *k, const void *v, gdn_dtype dtype,
                                  const float *g, const float *beta, float *state_pool, int64_t n_slots,
                                  const int32_t *slots, const int32_t *slots_host, float *o,
-                                 int64_t B, int32_t H, int32_t dk, int32_t dv, void *stream);
+                                 int64_t B, int32_t H, int32_t dk, int32_t dv, int32_t variant, void *stream);
 
 /* Activation after the pre-processing convolution. */
 typedef enum { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_activation;

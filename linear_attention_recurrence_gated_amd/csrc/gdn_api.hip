@@ -56,6 +56,8 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t elem_bytes(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
 
+int erase_of(int32_t variant) { return (variant & GDN_VARIANT_NO_ERASE) ? 0 : 1; }
+
 struct Range {
     const void *p;
     size_t n;
@@ -176,9 +178,11 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
                        const float *beta, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
                        int64_t total_tokens, int32_t H, int32_t dk, int32_t dv, const float *initial_state,
                        float *o, float *final_state, int32_t chunk, void *workspace, size_t workspace_bytes,
-                       void *stream) {
+                       int32_t variant, void *stream) {
     const Marks marks = take_marks();
     if (dtype != GDN_BF16 && dtype != GDN_FP32) return fail(GDN_ERR_DTYPE, "prefill: dtype %d", (int)dtype);
+    if (variant & ~GDN_VARIANT_MASK) return fail(GDN_ERR_UNSUPPORTED, "prefill: variant %d", variant);
+    if (variant & GDN_VARIANT_NO_GATE) g = nullptr;  // ignored: the ungated rule
     if (n_seq < 0 || total_tokens < 0 || H <= 0 || total_tokens > (int64_t)INT32_MAX)
         return fail(GDN_ERR_SHAPE, "prefill: n_seq=%lld total_tokens=%lld H=%d", (long long)n_seq,
                     (long long)total_tokens, H);
@@ -205,7 +209,7 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
     const size_t sbytes = gdn_state_bytes(n_seq, H, dk, dv);
     if (n_seq > 0 && sbytes == 0) return fail(GDN_ERR_SHAPE, "prefill: state size overflows");
     if (n_seq > 0 && !final_state) return fail(GDN_ERR_NULL, "prefill: final_state is NULL");
-    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
+    if (total_tokens > 0 && (!q || !k || !v || (!g && !(variant & GDN_VARIANT_NO_GATE)) || !beta || !o))
         return fail(GDN_ERR_NULL, "prefill: q, k, v, g, beta and o are required when total_tokens > 0");
     const size_t eb = elem_bytes(dtype);
     const size_t N = (size_t)total_tokens;
@@ -241,24 +245,27 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
             if (overlap({workspace, need}, in)) return fail(GDN_ERR_ALIAS, "prefill: workspace overlaps an argument");
         return hip_status(gdn::launch_prefill_chunked(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, n_seq,
                                                       total_tokens, H, initial_state, o, final_state, workspace,
-                                                      marks.ev, st),
+                                                      erase_of(variant), marks.ev, st),
                           "prefill (chunked) launch");
     }
     return hip_status(gdn::launch_prefill_serial(dtype == GDN_BF16, dk, q, k, v, g, beta, cu_seqlens, n_seq,
-                                                 total_tokens, H, initial_state, o, final_state, marks.ev, st),
+                                                 total_tokens, H, initial_state, o, final_state,
+                                                 erase_of(variant), marks.ev, st),
                       "prefill (serial) launch");
 }
 
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtype dtype, const float *g,
                            const float *beta, float *state, float *o, int64_t B, int32_t H, int32_t dk, int32_t dv,
-                           void *stream) {
+                           int32_t variant, void *stream) {
     if (dtype != GDN_BF16 && dtype != GDN_FP32) return fail(GDN_ERR_DTYPE, "decode_step: dtype %d", (int)dtype);
+    if (variant & ~GDN_VARIANT_MASK) return fail(GDN_ERR_UNSUPPORTED, "decode_step: variant %d", variant);
+    if (variant & GDN_VARIANT_NO_GATE) g = nullptr;
     if (B < 0 || H <= 0 || B * (int64_t)H > (int64_t)UINT32_MAX)
         return fail(GDN_ERR_SHAPE, "decode_step: B=%lld H=%d", (long long)B, H);
     if (!supported_d(dk, dv)) return fail(GDN_ERR_UNSUPPORTED, "decode_step: dk=%d dv=%d not supported", dk, dv);
     if (B == 0) return ok();
-    if (!q || !k || !v || !g || !beta || !state || !o)
-        return fail(GDN_ERR_NULL, "decode_step: every pointer is required");
+    if (!q || !k || !v || (!g && !(variant & GDN_VARIANT_NO_GATE)) || !beta || !state || !o)
+        return fail(GDN_ERR_NULL, "decode_step: every pointer is required (g may be NULL without the gate)");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16) || !aligned(o, 16))
         return fail(GDN_ERR_ALIGN, "decode_step: q, k, v, state and o must be 16-byte aligned");
     if (!aligned(g, 4) || !aligned(beta, 4)) return fail(GDN_ERR_ALIGN, "decode_step: g, beta must be 4-byte aligned");
@@ -270,23 +277,25 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtyp
     for (Range in : {rq, rk, rv, rg, rb})
         if (overlap(rs, in)) return fail(GDN_ERR_ALIAS, "decode_step: state overlaps an input");
     return hip_status(gdn::launch_decode(dtype == GDN_BF16, dk, q, k, v, g, beta, state, o, (int64_t)BH, H, nullptr,
-                                         0, (hipStream_t)stream),
+                                         0, erase_of(variant), (hipStream_t)stream),
                       "decode_step launch");
 }
 
 gdn_status gdn_decode_step_slots(const void *q, const void *k, const void *v, gdn_dtype dtype, const float *g,
                                  const float *beta, float *state_pool, int64_t n_slots, const int32_t *slots,
                                  const int32_t *slots_host, float *o, int64_t B, int32_t H, int32_t dk, int32_t dv,
-                                 void *stream) {
+                                 int32_t variant, void *stream) {
     if (dtype != GDN_BF16 && dtype != GDN_FP32)
         return fail(GDN_ERR_DTYPE, "decode_step_slots: dtype %d", (int)dtype);
+    if (variant & ~GDN_VARIANT_MASK) return fail(GDN_ERR_UNSUPPORTED, "decode_step_slots: variant %d", variant);
+    if (variant & GDN_VARIANT_NO_GATE) g = nullptr;
     if (B < 0 || H <= 0 || n_slots < 0 || B * (int64_t)H > (int64_t)UINT32_MAX || n_slots > (int64_t)INT32_MAX)
         return fail(GDN_ERR_SHAPE, "decode_step_slots: B=%lld H=%d n_slots=%lld", (long long)B, H,
                     (long long)n_slots);
     if (!supported_d(dk, dv))
         return fail(GDN_ERR_UNSUPPORTED, "decode_step_slots: dk=%d dv=%d not supported", dk, dv);
     if (B == 0) return ok();
-    if (!q || !k || !v || !g || !beta || !o || !slots)
+    if (!q || !k || !v || (!g && !(variant & GDN_VARIANT_NO_GATE)) || !beta || !o || !slots)
         return fail(GDN_ERR_NULL, "decode_step_slots: q, k, v, g, beta, slots and o are required");
     if (n_slots > 0 && !state_pool) return fail(GDN_ERR_NULL, "decode_step_slots: state_pool is NULL");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state_pool, 16) || !aligned(o, 16))
@@ -315,7 +324,7 @@ gdn_status gdn_decode_step_slots(const void *q, const void *k, const void *v, gd
     for (Range in : {rq, rk, rv, rg, rb, rsl})
         if (overlap(rs, in)) return fail(GDN_ERR_ALIAS, "decode_step_slots: state_pool overlaps an input");
     return hip_status(gdn::launch_decode(dtype == GDN_BF16, dk, q, k, v, g, beta, state_pool, o, (int64_t)BH, H,
-                                         slots, n_slots, (hipStream_t)stream),
+                                         slots, n_slots, erase_of(variant), (hipStream_t)stream),
                       "decode_step_slots launch");
 }
 

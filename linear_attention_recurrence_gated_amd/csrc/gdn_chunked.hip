@@ -252,7 +252,8 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
                                                     const float *__restrict__ g, const float *__restrict__ beta,
                                                     const int32_t *__restrict__ cu,
                                                     const int32_t *__restrict__ chunk_base, int n_seq,
-                                                    int64_t total_tokens, int H, char *__restrict__ recs) {
+                                                    int64_t total_tokens, int H, int erase,
+                                                    char *__restrict__ recs) {
     const int64_t gc = blockIdx.x / H;
     const int h = blockIdx.x % H;
     int64_t t0;
@@ -271,8 +272,8 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
     dma_rows(S.QT, q + cbase, rs, n, lane, wave, 4);
     if (wave == 0) {  // gate prefix sums and the record's gate factors
         const int64_t off = (t0 + min(lane, n - 1)) * H + h;
-        const float gl = g[off], bl = beta[off];
-        const float lam = lane < n ? __logf(fmaxf(gl, FLT_MIN)) : 0.f;
+        const float gl = g ? g[off] : 1.f, bl = beta[off];  // no g: the ungated rule
+        const float lam = (lane < n && g) ? __logf(fmaxf(gl, FLT_MIN)) : 0.f;
         const float bt = lane < n ? bl : 0.f;
         const float G = wave_inclusive_scan(lam, lane);
         const float Gm1 = __shfl_up(G, 1, 64);
@@ -282,7 +283,9 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
         float *gate = reinterpret_cast<float *>(rec + REC_GATE);
         gate[GATE_EG + lane] = __expf(G);
         gate[GATE_BW + lane] = bt * __expf(G63 - G);
-        gate[GATE_EGM1 + lane] = lane > 0 ? __expf(Gm1) : 1.f;
+        // without the erase term nothing is recalled from the entering state:
+        // Y = V - 0 X = V, and L = 0 below makes T = I, so U = V
+        gate[GATE_EGM1 + lane] = !erase ? 0.f : lane > 0 ? __expf(Gm1) : 1.f;
         if (lane == 63) gate[GATE_EGN] = __expf(G63);
     }
     wait_all_vmem();
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * ta + 4 * g4 + e;
                 const float gtm1 = t > 0 ? S.G[t - 1] : 0.f;
-                acc[e] = (s < t) ? bs * __expf(gtm1 - gs) * acc[e] : 0.f;
+                acc[e] = (s < t && erase) ? bs * __expf(gtm1 - gs) * acc[e] : 0.f;
             }
             if (j < 3) Lr[j] = acc;
         } else if (i < 16) {
@@ -1000,7 +1003,7 @@ size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int 
 hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, const float *g, const float *beta,
                                   const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
                                   int64_t total_tokens, int H, const float *initial_state, float *o,
-                                  float *final_state, void *workspace, const hipEvent_t *marks,
+                                  float *final_state, void *workspace, int erase, const hipEvent_t *marks,
                                   hipStream_t stream) {
     const WsLayout L = ws_layout(total_tokens, n_seq, H);
     hipError_t e = record_mark(marks[0], stream);
@@ -1021,7 +1024,7 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     if (n_chunks > 0) {
         hipLaunchKernelGGL(k_chunk_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream,
                            static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), g, beta, cu_seqlens,
-                           chunk_base, (int)n_seq, total_tokens, H, recs);
+                           chunk_base, (int)n_seq, total_tokens, H, erase, recs);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -12,7 +12,7 @@ namespace gdn {
 // One decode step for B*H heads (in-place state update).
 hipError_t launch_decode(bool bf16, int d, const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, float *o, int64_t BH, int H, const int32_t *slots,
-                         int64_t n_slots, hipStream_t stream);
+                         int64_t n_slots, int erase, hipStream_t stream);
 
 // marks[3]: events (or nullptr) recorded on `stream` before the first kernel,
 // after the state-independent kernels and after the state chain.
@@ -23,7 +23,7 @@ hipError_t record_mark(hipEvent_t ev, hipStream_t stream);
 hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k, const void *v,
                                  const float *g, const float *beta, const int32_t *cu_seqlens,
                                  int64_t n_seq, int64_t total_tokens, int H,
-                                 const float *initial_state, float *o, float *final_state,
+                                 const float *initial_state, float *o, float *final_state, int erase,
                                  const hipEvent_t *marks, hipStream_t stream);
 
 // Chunkwise-parallel prefill (64-token chunks, d = 128, bf16 q/k/v).
@@ -32,7 +32,7 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v,
                                   const float *g, const float *beta, const int32_t *cu_seqlens,
                                   const int32_t *cu_seqlens_host, int64_t n_seq,
                                   int64_t total_tokens, int H, const float *initial_state,
-                                  float *o, float *final_state, void *workspace,
+                                  float *o, float *final_state, void *workspace, int erase,
                                   const hipEvent_t *marks, hipStream_t stream);
 
 // Pre-processing: conv (4 taps) + optional SiLU + L2 norm of q, k + gate maps,

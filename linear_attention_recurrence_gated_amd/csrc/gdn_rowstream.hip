@@ -37,12 +37,13 @@ struct RowLayout {
 // slots: NULL for state [B][H][dv][dk]; else row b of the batch uses state
 // slot slots[b] of a pool [n_slots][H][dv][dk], and a row whose slot lies
 // outside [0, n_slots) is padding: its o row is zeroed, no state is touched.
+// g == NULL: no gate (g = 1).  erase == 0: no recall term (c = beta v).
 template <typename TIn, int D, int NW, bool NT>
 __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                          const TIn *__restrict__ v, const float *__restrict__ g,
                                                          const float *__restrict__ beta, float *__restrict__ state,
                                                          float *__restrict__ o, const int32_t *__restrict__ slots,
-                                                         int64_t n_slots, int H) {
+                                                         int64_t n_slots, int H, int erase) {
     using L = RowLayout<D>;
     constexpr int RPW = D / NW;
     constexpr int PASSES = (RPW + L::RPP - 1) / L::RPP;
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__
     const TIn *qp = q + bh * D;
     const float4 k0 = In<TIn>::load4(kp + c0), k1 = In<TIn>::load4(kp + c1);
     const float4 q0 = In<TIn>::load4(qp + c0), q1 = In<TIn>::load4(qp + c1);
-    const float gt = g[bh], bt = beta[bh];
+    const float gt = g ? g[bh] : 1.f, bt = beta[bh];
     float *S = state + sh * (int64_t)D * D;
 
     float4 s0[PASSES], s1[PASSES];
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__
         const int row = wave * RPW + rloc;
         const float a = group_sum<L::LPR>(dot4(s0[p], k0) + dot4(s1[p], k1));
         const float b = group_sum<L::LPR>(dot4(s0[p], q0) + dot4(s1[p], q1));
-        const float c = bt * (vr[p] - a);
+        const float c = bt * (vr[p] - (erase ? a : 0.f));
         if (ok) {
             store_state4<NT>(S + row * D + c0, axpby4(gt, s0[p], c, k0));
             store_state4<NT>(S + row * D + c1, axpby4(gt, s1[p], c, k1));
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q
                                                        const float *__restrict__ beta,
                                                        const int32_t *__restrict__ cu_seqlens, int64_t total_tokens,
                                                        int H, const float *initial_state, float *__restrict__ o,
-                                                       float *final_state) {
+                                                       float *final_state, int erase) {
     using L = RowLayout<D>;
     constexpr int TILES = D / ROWS;
     constexpr int PASSES = (ROWS + L::RPP - 1) / L::RPP;
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q
         q1n = In<TIn>::load4(q + th * D + c1);
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) vn[p] = In<TIn>::load1(v + th * D + rowp[p]);
-        gn = g[th];
+        gn = g ? g[th] : 1.f;
         bn = beta[th];
     };
     if (t0 < t1) fetch(t0);
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q
         for (int p = 0; p < PASSES; ++p) {
             const float a = group_sum<L::LPR>(dot4(s0[p], k0) + dot4(s1[p], k1));
             const float b = group_sum<L::LPR>(dot4(s0[p], q0) + dot4(s1[p], q1));
-            const float c = bt * (vr[p] - a);
+            const float c = bt * (vr[p] - (erase ? a : 0.f));
             s0[p] = axpby4(gt, s0[p], c, k0);
             s1[p] = axpby4(gt, s1[p], c, k1);
             if (okp[p] && lr == 0) orow[rowp[p]] = gt * b + c * kq;
@@ -195,25 +196,27 @@ constexpr int64_t DECODE_NT_MIN_BYTES = int64_t(32) << 20;
 template <typename TIn, int D>
 static hipError_t decode_d(const void *q, const void *k, const void *v, const float *g, const float *beta,
                            float *state, float *o, int64_t BH, int H, const int32_t *slots, int64_t n_slots,
-                           hipStream_t stream) {
+                           int erase, hipStream_t stream) {
     constexpr int NW = D >= 64 ? 4 : 1;
     if (BH * D * D * 4 >= DECODE_NT_MIN_BYTES)
         hipLaunchKernelGGL((k_decode_step<TIn, D, NW, true>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
-                           (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o, slots, n_slots, H);
+                           (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o, slots, n_slots, H,
+                           erase);
     else
         hipLaunchKernelGGL((k_decode_step<TIn, D, NW, false>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
-                           (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o, slots, n_slots, H);
+                           (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o, slots, n_slots, H,
+                           erase);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(bool bf16, int d, const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, float *o, int64_t BH, int H, const int32_t *slots,
-                         int64_t n_slots, hipStream_t stream) {
+                         int64_t n_slots, int erase, hipStream_t stream) {
     if (BH == 0) return hipSuccess;
 #define GDN_DEC(D)                                                                                      \
     case D:                                                                                             \
-        return bf16 ? decode_d<uint16_t, D>(q, k, v, g, beta, state, o, BH, H, slots, n_slots, stream) \
-                    : decode_d<float, D>(q, k, v, g, beta, state, o, BH, H, slots, n_slots, stream);
+        return bf16 ? decode_d<uint16_t, D>(q, k, v, g, beta, state, o, BH, H, slots, n_slots, erase, stream) \
+                    : decode_d<float, D>(q, k, v, g, beta, state, o, BH, H, slots, n_slots, erase, stream);
     switch (d) {
         GDN_DEC(16)
         GDN_DEC(32)
@@ -227,18 +230,18 @@ hipError_t launch_decode(bool bf16, int d, const void *q, const void *k, const v
 template <typename TIn, int D>
 static hipError_t serial_d(const void *q, const void *k, const void *v, const float *g, const float *beta,
                            const int32_t *cu, int64_t n_seq, int64_t total, int H, const float *s_in, float *o,
-                           float *s_out, hipStream_t stream) {
+                           float *s_out, int erase, hipStream_t stream) {
     constexpr int ROWS = D >= 32 ? 32 : D;
     const int64_t blocks = n_seq * H * (D / ROWS);
     hipLaunchKernelGGL((k_prefill_serial<TIn, D, ROWS>), dim3((unsigned)blocks), dim3(64), 0, stream,
-                       (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, cu, total, H, s_in, o, s_out);
+                       (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, cu, total, H, s_in, o, s_out, erase);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k, const void *v, const float *g,
                                  const float *beta, const int32_t *cu_seqlens, int64_t n_seq,
                                  int64_t total_tokens, int H, const float *initial_state, float *o,
-                                 float *final_state, const hipEvent_t *marks, hipStream_t stream) {
+                                 float *final_state, int erase, const hipEvent_t *marks, hipStream_t stream) {
     if (n_seq == 0) return hipSuccess;
     hipError_t e = record_mark(marks[0], stream);
     if (e == hipSuccess) e = record_mark(marks[1], stream);
@@ -246,9 +249,9 @@ hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k,
 #define GDN_SER(D)                                                                                         \
     case D:                                                                                                \
         e = bf16 ? serial_d<uint16_t, D>(q, k, v, g, beta, cu_seqlens, n_seq, total_tokens, H,             \
-                                         initial_state, o, final_state, stream)                            \
+                                         initial_state, o, final_state, erase, stream)                     \
                  : serial_d<float, D>(q, k, v, g, beta, cu_seqlens, n_seq, total_tokens, H,                \
-                                      initial_state, o, final_state, stream);                              \
+                                      initial_state, o, final_state, erase, stream);                       \
         break;
     switch (d) {
         GDN_SER(16)

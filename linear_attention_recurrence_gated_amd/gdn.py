@@ -23,6 +23,8 @@ LIB_PATH = os.path.join(HERE, "libgdn.so")
 
 GDN_BF16, GDN_FP32 = 0, 1
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
+# variants (flags): the gated delta rule, no gate (g = 1), no erase term (linear-attention write)
+GDN_VARIANT_GATED_DELTA, GDN_VARIANT_NO_GATE, GDN_VARIANT_NO_ERASE = 0, 1, 2
 CHUNK_AUTO, CHUNK_SERIAL, CHUNK_64 = 0, 1, 64
 
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
@@ -38,10 +40,10 @@ SIGNATURES = {
     "gdn_state_reset": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _i32, _vp]),
     "gdn_prefill_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32, _i32, _i32]),
     "gdn_prefill": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32,
-                           _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
-    "gdn_decode_step": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+                           _vp, _vp, _vp, _i32, _vp, _sz, _i32, _vp]),
+    "gdn_decode_step": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp]),
     "gdn_decode_step_slots": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i32, _i32,
-                                     _i32, _vp]),
+                                     _i32, _i32, _vp]),
     "gdn_prefill_set_marks": (_i32, [ctypes.POINTER(_vp), _i32]),
     "gdn_preprocess": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
                               _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -143,14 +145,16 @@ def state_reset(state, slots=None, stream=None):
 
 
 def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=CHUNK_AUTO,
-            cu_seqlens_device=None, out=None, final_state=None, workspace=None, stream=None):
+            cu_seqlens_device=None, out=None, final_state=None, workspace=None, stream=None,
+            variant=GDN_VARIANT_GATED_DELTA):
     """Chunkwise (or token-serial) prefill of a packed batch.
 
     q, k: [N, H, dk]; v: [N, H, dv] (bf16 or fp32, device); g, beta: [N, H] fp32.
     cu_seqlens: host offsets (list, numpy or CPU tensor) of the packed sequences,
     or None for one sequence; cu_seqlens_device: optional device int32 copy.
     initial_state: [n_seq, H, dv, dk] fp32 or None (zeros); it may be the same
-    tensor as final_state.  Returns (o [N, H, dv] fp32, final_state).
+    tensor as final_state.  variant: GDN_VARIANT_* flags (g may be None with
+    GDN_VARIANT_NO_GATE).  Returns (o [N, H, dv] fp32, final_state).
     """
     import torch
     N, H, dk = k.shape
@@ -185,7 +189,7 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=CHUNK_A
         _dev_ptr(cu_dev, "cu_seqlens_device", torch.int32), cu_host_ptr, n_seq, N, H, dk, dv,
         _dev_ptr(initial_state, "initial_state", torch.float32),
         _dev_ptr(out, "out", torch.float32), _dev_ptr(final_state, "final_state", torch.float32),
-        chunk, ws_ptr, ws_len, _stream(dev, stream)))
+        chunk, ws_ptr, ws_len, variant, _stream(dev, stream)))
     return out, final_state
 
 
@@ -201,9 +205,10 @@ def prefill_set_marks(events):
     _check(lib().gdn_prefill_set_marks(handles, len(events)))
 
 
-def decode_step(q, k, v, g, beta, state, out=None, stream=None):
+def decode_step(q, k, v, g, beta, state, out=None, stream=None, variant=GDN_VARIANT_GATED_DELTA):
     """One token per sequence: q, k [B, H, dk], v [B, H, dv], g, beta [B, H];
-    state [B, H, dv, dk] fp32 updated in place.  Returns o [B, H, dv] fp32."""
+    state [B, H, dv, dk] fp32 updated in place.  variant: GDN_VARIANT_* flags.
+    Returns o [B, H, dv] fp32."""
     import torch
     B, H, dk = k.shape
     dv = v.shape[2]
@@ -213,7 +218,7 @@ def decode_step(q, k, v, g, beta, state, out=None, stream=None):
         _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k),
         _dev_ptr(g, "g", torch.float32), _dev_ptr(beta, "beta", torch.float32),
         _dev_ptr(state, "state", torch.float32), _dev_ptr(out, "out", torch.float32),
-        B, H, dk, dv, _stream(k.device, stream)))
+        B, H, dk, dv, variant, _stream(k.device, stream)))
     return out
 
 
@@ -267,7 +272,8 @@ def preprocess(xq, xk, xv, conv_w, a_logit, b_logit, gate_bias=None, cu_seqlens=
     return q, k, v, g, beta, conv_state_out
 
 
-def decode_step_slots(q, k, v, g, beta, state_pool, slots, slots_host="auto", out=None, stream=None):
+def decode_step_slots(q, k, v, g, beta, state_pool, slots, slots_host="auto", out=None, stream=None,
+                      variant=GDN_VARIANT_GATED_DELTA):
     """One token for each of B requests; row b updates state_pool[slots[b]]
     ([n_slots, H, dv, dk] fp32) in place; slots[b] = -1 marks a padding row
     (o row zeroed).  slots: device int32 [B].  slots_host: "auto" copies slots
@@ -291,5 +297,5 @@ def decode_step_slots(q, k, v, g, beta, state_pool, slots, slots_host="auto", ou
         _dev_ptr(g, "g", torch.float32), _dev_ptr(beta, "beta", torch.float32),
         _dev_ptr(state_pool, "state_pool", torch.float32), n_slots, _dev_ptr(slots, "slots", torch.int32),
         None if host is None else host.ctypes.data_as(ctypes.c_void_p),
-        _dev_ptr(out, "out", torch.float32), B, H, dk, dv, _stream(k.device, stream)))
+        _dev_ptr(out, "out", torch.float32), B, H, dk, dv, variant, _stream(k.device, stream)))
     return out

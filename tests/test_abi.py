@@ -83,7 +83,7 @@ def _prefill(**kw):
     L = gdn.lib()
     st = L.gdn_prefill(a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"], a["cu"], a["cu_host"], a["n_seq"],
                        a["N"], a["H"], a["dk"], a["dv"], a["s0"], a["o"], a["s1"], a["chunk"], a["ws"],
-                       a["ws_bytes"], None)
+                       a["ws_bytes"], a.get("variant", 0), None)
     return st, L.gdn_last_error().decode()
 
 
@@ -106,6 +106,9 @@ def _host(arr):
     (dict(n_seq=2), 5),                      # no cu_seqlens but more than one sequence
     (dict(o=FAKE), 8),                       # o on top of q
     (dict(s1=FAKE), 8),                      # final state on top of q
+    (dict(variant=4), 7),                    # unknown variant bit
+    (dict(g=None, variant=2), 1),            # g is needed unless the gate is off
+    (dict(g=None, variant=1, q=None), 1),    # without the gate g may be NULL, q may not
 ])
 def test_prefill_validation(kw, code):
     st, msg = _prefill(**kw)
@@ -134,7 +137,7 @@ def test_decode_validation():
                  H=2, dk=128, dv=128)
         a.update(kw)
         return L.gdn_decode_step(a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"], a["s"], a["o"], a["B"],
-                                 a["H"], a["dk"], a["dv"], None)
+                                 a["H"], a["dk"], a["dv"], a.get("variant", 0), None)
 
     assert call(dtype=9) == 3
     assert call(B=-1) == 2
@@ -144,6 +147,9 @@ def test_decode_validation():
     assert call(o=FAKE) == 8
     assert call(s=FAKE) == 8
     assert call(B=0) == 0  # nothing to do, nothing enqueued
+    assert call(variant=8) == 7
+    assert call(g=None) == 1
+    assert call(g=None, variant=1, o=FAKE) == 8  # g may be NULL without the gate; o on q still caught
 
 
 def test_state_calls_validation():
@@ -229,7 +235,8 @@ def _decode_slots(**kw):
     a.update(kw)
     L = gdn.lib()
     st = L.gdn_decode_step_slots(a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"], a["pool"], a["n_slots"],
-                                 a["slots"], a["slots_host"], a["o"], a["B"], a["H"], a["dk"], a["dv"], None)
+                                 a["slots"], a["slots_host"], a["o"], a["B"], a["H"], a["dk"], a["dv"],
+                                 a.get("variant", 0), None)
     return st, L.gdn_last_error().decode()
 
 
@@ -244,6 +251,8 @@ def _decode_slots(**kw):
     (dict(o=FAKE * 7 + 8), 4),
     (dict(o=FAKE * 6), 8),                   # o on top of slots
     (dict(pool=FAKE * 2), 8),                # pool on top of k
+    (dict(variant=16), 7),
+    (dict(g=None), 1),
 ])
 def test_decode_slots_validation(kw, code):
     st, msg = _decode_slots(**kw)
