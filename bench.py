@@ -178,6 +178,42 @@ def bench_decode(torch, gdn, w, steps, rotate):
     return ms
 
 
+def bench_scan(torch, gdn, w, steps, warmup):
+    """One sequence with few heads: the per-GPU share of the one-layer prefill
+    when its 48 heads are split over 8 GPUs (H = 6, T = 4096), and the same at
+    T = 16384; each timed with the one-chain form and with the chunk-level
+    scan (event-bracketed calls, inputs resident).  Returns a dict."""
+    import numpy as np
+    dev = "cuda:0"
+    out = {}
+    for T_ in (T, 4 * T):
+        inp = w.make_prefill([T_], H=6, d=D, seed=w.SEED_BASE + 7, packed=False)
+        q, k, v = (w.to_torch(x, "bf16", dev) for x in (inp.q, inp.k, inp.v))
+        g = torch.from_numpy(inp.g).to(dev)
+        beta = torch.from_numpy(inp.beta).to(dev)
+        row = {}
+        for name, ch in (("chain", gdn.CHUNK_64_CHAIN), ("scan", gdn.CHUNK_64_SCAN)):
+            o = torch.empty((T_, 6, D), dtype=torch.float32, device=dev)
+            st = torch.empty((1, 6, D, D), dtype=torch.float32, device=dev)
+            ws = torch.empty(gdn.prefill_workspace_bytes(T_, 1, 6, D, D, gdn.GDN_BF16, ch), dtype=torch.uint8,
+                             device=dev)
+            call = lambda: gdn.prefill(q, k, v, g, beta, chunk=ch, out=o, final_state=st, workspace=ws)
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for a, b in ev:
+                a.record()
+                call()
+                b.record()
+            torch.cuda.synchronize()
+            row[name + "_ms"] = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        row["speedup"] = row["chain_ms"] / row["scan_ms"]
+        row["scan_tokens_per_s"] = T_ / (row["scan_ms"] / 1e3)
+        out[f"H6_T{T_}"] = row
+    return out
+
+
 def bench_decode_slots(torch, gdn, w, steps, rotate):
     """Serving form of the decode step: the 64 rows of the batch take a fixed
     random permutation of 64 of the 128 slots of a state pool (one pool per
@@ -325,7 +361,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of parts to time alone (prefill, decode, decode_slots, preprocess, copy), one JSON line "
+                    help="comma list of parts to time alone (prefill, decode, decode_slots, preprocess, scan, copy), one JSON "
+                         "line "
                          "each, for "
                          "profiling runs; 'copy' is the byte-counter calibration copy")
     ap.add_argument("--warm", action="store_true",
@@ -349,7 +386,7 @@ def main():
 
     if args.only:
         parts = args.only.split(",")
-        bad = [p for p in parts if p not in ("prefill", "decode", "decode_slots", "preprocess", "copy")]
+        bad = [p for p in parts if p not in ("prefill", "decode", "decode_slots", "preprocess", "scan", "copy")]
         if bad:
             ap.error(f"--only: unknown part(s) {bad}")
         for part in parts:
@@ -364,6 +401,8 @@ def main():
                 ds_ms, dg_ms = bench_decode_slots(torch, gdn, w, args.decode_steps, args.rotate)
                 print(json.dumps({"only": "decode_slots", "ms_per_step": mean(ds_ms),
                                   "graph_replay_ms_per_step": mean(dg_ms)}), flush=True)
+            elif part == "scan":
+                print(json.dumps({"only": "scan", **bench_scan(torch, gdn, w, args.steps, args.warmup)}), flush=True)
             elif part == "preprocess":
                 pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
                 print(json.dumps({"only": "preprocess", "ms_per_call": mean(pre_ms)}), flush=True)
@@ -374,6 +413,7 @@ def main():
     dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
     pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
     ds_ms, dg_ms = bench_decode_slots(torch, gdn, w, args.decode_steps, args.rotate)
+    scan = bench_scan(torch, gdn, w, min(args.steps, 20), args.warmup)
 
     step_ms = mean(ms)
     tok_s = T / (step_ms / 1e3)
@@ -437,6 +477,8 @@ def main():
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                                 "traffic": load_traffic("k_decode_step")}},
         "preprocess": pre_entry(pre_ms),
+        "scan": {"workload": "one sequence, H = 6 (48 heads over 8 GPUs), d = 128, bf16: one-chain form vs the "
+                             "chunk-level scan", **scan},
         "decode_slots": {"ms_per_step": mean(ds_ms), "p50_ms": pct(ds_ms, 50), "p99_ms": pct(ds_ms, 99),
                          "value": dec_bytes / (mean(ds_ms) / 1e3) / 1e9, "unit": "GB/s",
                          "frac_hbm_peak": dec_bytes / (mean(ds_ms) / 1e3) / 1e9 / HBM_PEAK_GBS,

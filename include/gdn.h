@@ -60,7 +60,13 @@ typedef enum {
 /* Prefill algorithms (the `chunk` argument of gdn_prefill). */
 #define GDN_CHUNK_AUTO 0     /* chunked (64) where built, else token-serial */
 #define GDN_CHUNK_SERIAL 1   /* token-serial: one fixed-size update per token */
-#define GDN_CHUNK_64 64      /* chunkwise-parallel, 64-token chunks, MFMA (bf16 q/k/v, d = 128) */
+#define GDN_CHUNK_64 64      /* chunkwise-parallel, 64-token chunks, MFMA (bf16 q/k/v, d = 128);
+                                the library picks one of the two forms below */
+#define GDN_CHUNK_64_CHAIN 65 /* chunked; each (sequence, head) carries its state chunk to chunk */
+#define GDN_CHUNK_64_SCAN 66  /* chunked; one sequence cut into segments whose affine state maps
+                                 (S_out = S_in M + R) are formed in parallel and combined in order
+                                 (the chunk-parallel state accumulation of "Qwen3.8-27B 架构深读",
+                                 section 三); picked by GDN_CHUNK_64 for one sequence with few heads */
 
 /* Variants of the recurrence (the `variant` argument of gdn_prefill,
  * gdn_decode_step and gdn_decode_step_slots), from the equations of the
@@ -84,7 +90,8 @@ typedef enum {
 size_t gdn_state_bytes(int64_t n_seq, int32_t H, int32_t dk, int32_t dv);
 
 /* Which algorithm gdn_prefill would run for these arguments:
- * GDN_CHUNK_SERIAL, GDN_CHUNK_64, or 0 if the combination is not supported. */
+ * GDN_CHUNK_SERIAL, GDN_CHUNK_64 (or the explicit GDN_CHUNK_64_CHAIN /
+ * GDN_CHUNK_64_SCAN asked for), or 0 if the combination is not supported. */
 int32_t gdn_prefill_algorithm(gdn_dtype dtype, int32_t dk, int32_t dv, int32_t chunk);
 
 /* Set a state before any token arrives ("attention and memory", stethem.com,
@@ -121,7 +128,8 @@ size_t gdn_prefill_workspace_bytes(int64_t total_tokens, int64_t n_seq, int32_t 
  *                             not otherwise overlap it.
  *   o             [N][H][dv]  fp32 output (must not overlap any input)
  *   final_state   [n_seq][H][dv][dk] fp32 output
- *   chunk         GDN_CHUNK_AUTO, GDN_CHUNK_SERIAL or GDN_CHUNK_64
+ *   chunk         GDN_CHUNK_AUTO, GDN_CHUNK_SERIAL, GDN_CHUNK_64, GDN_CHUNK_64_CHAIN or
+ *                 GDN_CHUNK_64_SCAN (one sequence of >= 128 tokens, else GDN_ERR_UNSUPPORTED)
  *   workspace     device scratch of at least gdn_prefill_workspace_bytes();
  *                 may be NULL when that is 0.  Its contents on entry do not matter.
  *   variant       GDN_VARIANT_* flags (0: the gated delta rule)

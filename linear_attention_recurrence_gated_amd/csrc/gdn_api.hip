@@ -58,6 +58,13 @@ size_t elem_bytes(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
 
 int erase_of(int32_t variant) { return (variant & GDN_VARIANT_NO_ERASE) ? 0 : 1; }
 
+bool is_chunked(int32_t algo) { return algo == GDN_CHUNK_64 || algo == GDN_CHUNK_64_CHAIN || algo == GDN_CHUNK_64_SCAN; }
+
+int chunked_mode(int32_t algo) {
+    return algo == GDN_CHUNK_64_CHAIN ? gdn::CHUNKED_CHAIN : algo == GDN_CHUNK_64_SCAN ? gdn::CHUNKED_SCAN
+                                                                                     : gdn::CHUNKED_AUTO;
+}
+
 struct Range {
     const void *p;
     size_t n;
@@ -78,6 +85,8 @@ int32_t pick_algorithm(gdn_dtype dtype, int32_t dk, int32_t dv, int32_t chunk) {
         case GDN_CHUNK_AUTO: return chunked_built ? GDN_CHUNK_64 : GDN_CHUNK_SERIAL;
         case GDN_CHUNK_SERIAL: return GDN_CHUNK_SERIAL;
         case GDN_CHUNK_64: return chunked_built ? GDN_CHUNK_64 : 0;
+        case GDN_CHUNK_64_CHAIN: return chunked_built ? GDN_CHUNK_64_CHAIN : 0;
+        case GDN_CHUNK_64_SCAN: return chunked_built ? GDN_CHUNK_64_SCAN : 0;
         default: return 0;
     }
 }
@@ -170,8 +179,9 @@ gdn_status gdn_state_reset(float *state, int64_t n_seq, int32_t H, int32_t dk, i
 size_t gdn_prefill_workspace_bytes(int64_t total_tokens, int64_t n_seq, int32_t H, int32_t dk, int32_t dv,
                                    gdn_dtype dtype, int32_t chunk) {
     if (total_tokens < 0 || n_seq < 0 || H <= 0) return 0;
-    if (pick_algorithm(dtype, dk, dv, chunk) != GDN_CHUNK_64) return 0;
-    return gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H);
+    const int32_t algo = pick_algorithm(dtype, dk, dv, chunk);
+    if (!is_chunked(algo)) return 0;
+    return gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H, chunked_mode(algo));
 }
 
 gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dtype, const float *g,
@@ -235,8 +245,10 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
 
     hipStream_t st = (hipStream_t)stream;
     if (n_seq == 0) return ok();
-    if (algo == GDN_CHUNK_64) {
-        const size_t need = gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H);
+    if (algo == GDN_CHUNK_64_SCAN && (n_seq != 1 || total_tokens < 2 * 64))
+        return fail(GDN_ERR_UNSUPPORTED, "prefill: the chunk-level scan takes one sequence of at least 128 tokens");
+    if (is_chunked(algo)) {
+        const size_t need = gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H, chunked_mode(algo));
         if (need > 0 && (!workspace || workspace_bytes < need))
             return fail(GDN_ERR_WORKSPACE, "prefill: workspace of %zu bytes needed, %zu given", need,
                         workspace ? workspace_bytes : (size_t)0);
@@ -245,7 +257,7 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
             if (overlap({workspace, need}, in)) return fail(GDN_ERR_ALIAS, "prefill: workspace overlaps an argument");
         return hip_status(gdn::launch_prefill_chunked(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, n_seq,
                                                       total_tokens, H, initial_state, o, final_state, workspace,
-                                                      erase_of(variant), marks.ev, st),
+                                                      erase_of(variant), chunked_mode(algo), marks.ev, st),
                           "prefill (chunked) launch");
     }
     return hip_status(gdn::launch_prefill_serial(dtype == GDN_BF16, dk, q, k, v, g, beta, cu_seqlens, n_seq,

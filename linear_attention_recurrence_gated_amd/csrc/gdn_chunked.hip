@@ -37,6 +37,11 @@
 //                  barrier per chunk).  Each compute wave owns 16 rows of S:
 //                  rows are independent, so the waves and workgroups of one
 //                  head never exchange data.
+//   k_chunk_chain_cs  the same with four workgroups per (sequence, head) and
+//                  the columns of S split over pairs of waves, for few pairs.
+//   k_scan_combine the chunk-level scan for one sequence with few heads
+//                  (three k_chunk_chain_cs passes over segments, then a short
+//                  ordered combine of their affine maps); see below.
 //
 // q, k and v chunks live in LDS as row tiles: 64 token rows of 256 bytes whose
 // 16-byte units are XOR-swizzled by (row & 15).  The swizzle is applied by the
@@ -44,6 +49,7 @@
 // destination), row fragments are read with 8/16-byte loads, and the
 // token-major fragments of K^T and V^T come from ds_read_b64_tr_b16, which
 // transposes 16-bit elements across each group of 16 lanes.
+#include <algorithm>
 #include <cfloat>
 #include <cstdlib>
 
@@ -81,11 +87,33 @@ static_assert(REC_BYTES % 256 == 0, "record layout");
 
 constexpr int TILE = C * DK * 2;  // one bf16 row tile: 16 KiB
 
-struct WsLayout {
-    size_t base_off, order_off, rec_off, total;
+// The chunk-level scan (one sequence, few heads): the sequence is cut into P
+// segments of cps chunks each (the last one possibly shorter).
+struct ScanPlan {
+    int P = 0, cps = 0;
 };
 
-WsLayout ws_layout(int64_t total_tokens, int64_t n_seq, int H) {
+constexpr int SCAN_MIN_SEGMENTS = 6;  // below this the three chain passes cost more than one chain
+
+ScanPlan scan_plan(int64_t total_tokens, int H, bool forced) {
+    ScanPlan sp;
+    const int64_t nc = (total_tokens + C - 1) / C;
+    const int64_t fit = 256 / ((int64_t)H * 4);  // segments whose column-split chains fill the CUs once
+    int64_t P = std::min<int64_t>(nc / 2, fit);
+    if (forced && nc >= 2) P = std::max<int64_t>(P, 2);
+    if (P < 2) return sp;
+    sp.cps = (int)((nc + P - 1) / P);
+    sp.P = (int)((nc + sp.cps - 1) / sp.cps);
+    return sp;
+}
+
+struct WsLayout {
+    size_t base_off, order_off, rec_off, total;
+    ScanPlan scan;                                                   // scan.P == 0: no scan
+    size_t seg_cu_off, seg_base_off, zero_off, r_off, m_off, sin_off;
+};
+
+WsLayout ws_layout(int64_t total_tokens, int64_t n_seq, int H, int scan) {  // scan: 0 no, 1 chosen, 2 forced
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     WsLayout L;
     L.base_off = 0;
@@ -93,6 +121,17 @@ WsLayout ws_layout(int64_t total_tokens, int64_t n_seq, int H) {
     L.rec_off = L.order_off + up((size_t)n_seq * 4);
     const size_t max_chunks = (size_t)((total_tokens + C - 1) / C + n_seq);
     L.total = L.rec_off + max_chunks * (size_t)H * REC_BYTES;
+    if (scan) {
+        L.scan = scan_plan(total_tokens, H, scan == 2);
+        const size_t P = (size_t)L.scan.P, states = up(P * H * DK * DK * sizeof(float));
+        L.seg_cu_off = L.total;
+        L.seg_base_off = L.seg_cu_off + up((P + 1) * 4);
+        L.zero_off = L.seg_base_off + up((P + 1) * 4);
+        L.r_off = L.zero_off + 256;
+        L.m_off = L.r_off + states;
+        L.sin_off = L.m_off + states;
+        L.total = L.sin_off + states;
+    }
     return L;
 }
 
@@ -248,12 +287,28 @@ __device__ __forceinline__ float4 t4(const char *qt, int t, int s4) {  // T[t][s
     return *reinterpret_cast<const float4 *>(qt + t * 256 + ((((s4 >> 2) ^ (t & 15)) << 4)));
 }
 
+// Segments of the chunk-level scan (cu == NULL: no scan): token and chunk
+// offsets of P segments of cps chunks, and a zero page; written by the first
+// workgroup of k_chunk_prep.
+struct ScanSegs {
+    int32_t *cu = nullptr, *base = nullptr;
+    uint32_t *zero_page = nullptr;
+    int P = 0, cps = 0;
+};
+
 __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                     const float *__restrict__ g, const float *__restrict__ beta,
                                                     const int32_t *__restrict__ cu,
                                                     const int32_t *__restrict__ chunk_base, int n_seq,
                                                     int64_t total_tokens, int H, int erase,
-                                                    char *__restrict__ recs) {
+                                                    char *__restrict__ recs, ScanSegs segs) {
+    if (blockIdx.x == 0 && segs.cu) {
+        for (int i = threadIdx.x; i <= segs.P; i += 256) {
+            segs.cu[i] = (int32_t)min((int64_t)i * segs.cps * C, total_tokens);
+            segs.base[i] = (int32_t)(i * segs.cps);
+        }
+        if (threadIdx.x < 64) segs.zero_page[threadIdx.x] = 0u;
+    }
     const int64_t gc = blockIdx.x / H;
     const int h = blockIdx.x % H;
     int64_t t0;
@@ -696,8 +751,8 @@ __device__ __forceinline__ u32x4_t vfrag(const char *tile, int ks, int col0, int
 // has exactly 16 loads in flight after its copies.
 static_assert(REC_PIECES == 25 && VC_BYTES / FRAG == 4, "copy assignment");
 __device__ __forceinline__ void cs_copies(ChainBufCS &B, char *scratch, const char *rec, const uint16_t *qc,
-                                          const uint16_t *kc, const uint16_t *vc, int rs, int n, int lane, int cw,
-                                          int half) {
+                                          const uint16_t *kc, const uint16_t *vc, int rs, int vrs, int n, int lane,
+                                          int cw, int half) {
     const int a0 = 8 * half, a1 = a0 + 8;  // loads a0 .. a1 - 1 of this wave's 16
     if (cw == 0) {
 #pragma unroll
@@ -712,7 +767,7 @@ __device__ __forceinline__ void cs_copies(ChainBufCS &B, char *scratch, const ch
                 __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + (16 + a) * FRAG + lane * 16),
                                                  (lds_void *)(B.rec + (16 + a) * FRAG), 16, 0, 0);
             } else if (a < REC_PIECES - 16 + 4) {
-                dma_vcols(B.V, vc, rs, n, lane, a - (REC_PIECES - 16));
+                dma_vcols(B.V, vc, vrs, n, lane, a - (REC_PIECES - 16));
             } else {
                 __builtin_amdgcn_global_load_lds(static_cast<const void *>(rec + lane * 16), (lds_void *)scratch, 16, 0,
                                                  0);
@@ -742,11 +797,14 @@ __device__ __forceinline__ const uint32_t *chunk_line(const char *rec, const uin
     return reinterpret_cast<const uint32_t *>(base + rowbase + (uint32_t)(min(row, n - 1) * rs + half * 64));
 }
 
+// vz: NULL, or a page of at least 64 zero bytes that stands in for every row
+// of v; the chain then runs the homogeneous part of the update (v = 0) from
+// S = I, and initial_state is not read.
 __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ seq_order,
     int n_seq, int64_t total_tokens, int H, const float *initial_state, float *__restrict__ o, float *final_state,
-    const char *__restrict__ recs) {
+    const char *__restrict__ recs, const uint16_t *__restrict__ vz) {
     const int bid = blockIdx.x;
     // All workgroups of one (sequence, head) share bid % 8, so they run on one XCD and share its L2.
     const int u = (bid / (8 * CS_TILES)) * 8 + (bid & 7);
@@ -772,7 +830,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             const int n = (int)min((int64_t)C, L - (int64_t)c * C);
             const int64_t rowbase = (t0 * H + h) * DK;
             cs_copies(sm.buf[c & 1], sm.scratch, recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q + rowbase,
-                      k + rowbase, v + rowbase + vcol0, rs, n, lane, cw, half);
+                      k + rowbase, vz ? vz : v + rowbase + vcol0, rs, vz ? 0 : rs, n, lane, cw, half);
         };
         // Touch chunk c: the first 16 bytes of each 128-byte line in this
         // workgroup's quarter of the lines (the four workgroups of a pair share
@@ -781,7 +839,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         // re-touch line 0, so every wave issues exactly one load.
         auto touch = [=](int c) {
             int line = tile + CS_TILES * (cw * 64 + lane);
-            if (line >= PF_LINES) line = 0;
+            if (line >= PF_LINES || (vz && line >= REC_BYTES / 128 + 4 * C)) line = 0;  // no v lines to touch
             const int64_t t0 = seq_t0 + (int64_t)c * C;
             const int n = (int)min((int64_t)C, L - (int64_t)c * C);
             const uint32_t *src = chunk_line(recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q, k, v,
@@ -829,8 +887,15 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     f32x4_t St[4];
     const int64_t sbase = ((int64_t)s * H + h) * DK * DK + (int64_t)(iw + r) * DK + 64 * hf;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        St[j] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + 16 * j + 4 * g4) : zero4();
+    for (int j = 0; j < 4; ++j) {
+        if (vz) {  // the homogeneous pass starts from S = I
+#pragma unroll
+            for (int e = 0; e < 4; ++e) St[j][e] = (iw + r == 16 * (4 * hf + j) + 4 * g4 + e) ? 1.f : 0.f;
+        } else {
+            St[j] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + 16 * j + 4 * g4)
+                                  : zero4();
+        }
+    }
     // output tiles of this wave: {0, 3} or {1, 2} (balanced P U work)
     const int ta = hf ? 1 : 0, tz = hf ? 2 : 3;
 
@@ -943,13 +1008,13 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
 hipError_t launch_chain_cs(const void *q, const void *k, const void *v, const int32_t *cu, const int32_t *chunk_base,
                            const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H,
                            const float *initial_state, float *o, float *final_state, const char *recs,
-                           hipStream_t stream) {
+                           hipStream_t stream, const uint16_t *vz = nullptr) {
     const int64_t units = n_seq * H;
     const int64_t grid = ((units + 7) / 8) * 8 * CS_TILES;
     hipLaunchKernelGGL(k_chunk_chain_cs, dim3((unsigned)grid), dim3(512), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), cu, chunk_base, seq_order, (int)n_seq, total_tokens, H,
-                       initial_state, o, final_state, recs);
+                       initial_state, o, final_state, recs, vz);
     return hipGetLastError();
 }
 
@@ -966,6 +1031,116 @@ hipError_t launch_chain(const void *q, const void *k, const void *v, const int32
                        static_cast<const uint16_t *>(v), cu, chunk_base, seq_order,
                        (int)n_seq, total_tokens, H, initial_state, o, final_state, recs);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Chunk-level scan for one sequence with few heads.  Over a segment of chunks
+// the state update is affine, S_out = S_in M + R ([GDN]'s recurrence is linear
+// in S with transitions g I - beta k k^T acting from the right).  Three
+// column-split chain passes over all segments at once, and a short sequential
+// combine:
+//   A1  every segment from S = 0 with the real v       -> R_j (its final state)
+//   A2  every segment from S = I with v = 0            -> M_j (the product of its transitions)
+//   combine  S_in(0) = S_0,  S_in(j+1) = S_in(j) M_j + R_j,  final state = S_in(P)
+//   D   every segment from S_in(j) with the real v     -> the outputs
+// The records of the per-chunk kernel serve all three passes unchanged.
+
+// combine: one 4-wave workgroup per (head, block of 16 state rows); the rows
+// of S are independent.  Wave w forms columns 32 w .. 32 w + 31 of
+// S_in(j) M_j + R_j on fp32 MFMA (v_mfma_f32_16x16x4f32: lane (g, r) holds
+// A[r][g] and B[g][r]; result rows 4 g + e of column r), as four independent
+// accumulator chains (two column tiles x two halves of k).  The M and R
+// values of step j + 1 are loaded while step j is formed.  The eight
+// workgroups of a head run on one XCD (block b runs on XCD b % 8) and touch
+// M and R of step j + 1 + SCAN_TOUCH ahead of use, each an eighth of M's
+// lines and its own rows of R, so that the loads hit in that XCD's L2.
+constexpr int SCAN_TOUCH = 3;
+
+__global__ __launch_bounds__(256) void k_scan_combine(int P, int H, const float *s0, const float *__restrict__ R,
+                                                      const float *__restrict__ M, float *__restrict__ s_in,
+                                                      float *final_state) {
+    const int bid = blockIdx.x;
+    const int h = (bid & 7) + 8 * (bid >> 6), rb = (bid >> 3) & 7;  // grid: 64 per group of 8 heads
+    if (h >= H) return;
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row0 = 16 * rb, c0 = 32 * wave;
+    const int64_t dd = (int64_t)DK * DK;
+    __shared__ float Srow[16][DK + 4];
+    __shared__ __attribute__((aligned(16))) char scratch[4 * 1024];  // landing area of the line touches
+
+    // lines of step j touched by this thread: tid < 64: line 8 tid + rb of M_j
+    // (an eighth of its 512); 64 <= tid < 128: line tid - 64 of this block's
+    // 16 rows of R_j (64 lines); the other lanes re-touch line rb of M_j.
+    auto touch = [&](int j) {
+        const int64_t sh = ((int64_t)j * H + h) * dd;
+        const float *src = tid < 64            ? M + sh + (int64_t)(8 * tid + rb) * 32
+                         : tid < 128           ? R + sh + (int64_t)row0 * DK + (int64_t)(tid - 64) * 32
+                                               : M + sh + (int64_t)rb * 32;
+        __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)(scratch + wave * 1024), 4, 0,
+                                         0);
+    };
+    for (int j = 1; j <= SCAN_TOUCH && j < P; ++j) touch(j);
+
+    // lane (g, r) of tile t needs M[4 ks + g][c0 + 16 t + r], ks = 0..31, and
+    // R[row0 + 4 g + e][c0 + 16 t + r]
+    float mc[2][DK / 4], rc[2][4], mn[2][DK / 4], rn[2][4];
+    auto load = [&](int j, float (&m)[2][DK / 4], float (&rr)[2][4]) {
+        const int64_t sh = ((int64_t)j * H + h) * dd;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int ks = 0; ks < DK / 4; ++ks) m[t][ks] = M[sh + (int64_t)(4 * ks + g4) * DK + c0 + 16 * t + r];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[t][e] = R[sh + (int64_t)(row0 + 4 * g4 + e) * DK + c0 + 16 * t + r];
+        }
+    };
+    load(0, mc, rc);
+    for (int i = tid; i < 16 * DK; i += 256) {  // S_in(0) = S_0: read before anything is written
+        const int rr = i / DK, cc = i % DK;
+        const float x = s0 ? s0[(int64_t)h * dd + (int64_t)(row0 + rr) * DK + cc] : 0.f;
+        Srow[rr][cc] = x;
+        s_in[(int64_t)h * dd + (int64_t)(row0 + rr) * DK + cc] = x;
+    }
+    __syncthreads();
+    for (int j = 0; j < P; ++j) {
+        if (j + 1 < P) load(j + 1, mn, rn);
+        if (j + 1 + SCAN_TOUCH < P) touch(j + 1 + SCAN_TOUCH);
+        f32x4_t acc[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            acc[t][0] = f32x4_t{rc[t][0], rc[t][1], rc[t][2], rc[t][3]};
+            acc[t][1] = zero4();
+        }
+#pragma unroll
+        for (int ks = 0; ks < DK / 8; ++ks) {
+            const float a0 = Srow[r][4 * ks + g4], a1 = Srow[r][DK / 2 + 4 * ks + g4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                acc[t][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, mc[t][ks], acc[t][0], 0, 0, 0);
+                acc[t][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, mc[t][DK / 8 + ks], acc[t][1], 0, 0, 0);
+            }
+        }
+        __syncthreads();  // every wave has read S_in(j)
+        float *dst = j + 1 < P ? s_in + ((int64_t)(j + 1) * H + h) * dd : final_state + (int64_t)h * dd;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 4 * g4 + e, cc = c0 + 16 * t + r;
+                const float x = acc[t][0][e] + acc[t][1][e];
+                Srow[rr][cc] = x;
+                dst[(int64_t)(row0 + rr) * DK + cc] = x;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int ks = 0; ks < DK / 4; ++ks) mc[t][ks] = mn[t][ks];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rc[t][e] = rn[t][e];
+        }
+    }
 }
 
 // Compute waves per chain workgroup (it has as many copy waves).  Each compute
@@ -996,16 +1171,23 @@ bool use_column_split(int64_t units) {
 
 }  // namespace
 
-size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H) {
-    return ws_layout(total_tokens, n_seq, H).total;
+// 0: one chain per (sequence, head); 1: the scan, chosen; 2: the scan, asked for.
+int scan_chosen(int mode, int64_t n_seq, int64_t total_tokens, int H) {
+    if (mode == CHUNKED_SCAN) return 2;
+    if (mode == CHUNKED_CHAIN || n_seq != 1) return 0;
+    return scan_plan(total_tokens, H, false).P >= SCAN_MIN_SEGMENTS ? 1 : 0;
+}
+
+size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H, int mode) {
+    return ws_layout(total_tokens, n_seq, H, scan_chosen(mode, n_seq, total_tokens, H)).total;
 }
 
 hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, const float *g, const float *beta,
                                   const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
                                   int64_t total_tokens, int H, const float *initial_state, float *o,
-                                  float *final_state, void *workspace, int erase, const hipEvent_t *marks,
-                                  hipStream_t stream) {
-    const WsLayout L = ws_layout(total_tokens, n_seq, H);
+                                  float *final_state, void *workspace, int erase, int mode,
+                                  const hipEvent_t *marks, hipStream_t stream) {
+    const WsLayout L = ws_layout(total_tokens, n_seq, H, scan_chosen(mode, n_seq, total_tokens, H));
     hipError_t e = record_mark(marks[0], stream);
     if (e != hipSuccess) return e;
     char *ws = static_cast<char *>(workspace);
@@ -1021,16 +1203,44 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     } else {
         n_chunks = (total_tokens + C - 1) / C;
     }
+    ScanSegs segs;
+    if (L.scan.P > 0) {
+        segs.cu = reinterpret_cast<int32_t *>(ws + L.seg_cu_off);
+        segs.base = reinterpret_cast<int32_t *>(ws + L.seg_base_off);
+        segs.zero_page = reinterpret_cast<uint32_t *>(ws + L.zero_off);
+        segs.P = L.scan.P;
+        segs.cps = L.scan.cps;
+    }
     if (n_chunks > 0) {
         hipLaunchKernelGGL(k_chunk_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream,
                            static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), g, beta, cu_seqlens,
-                           chunk_base, (int)n_seq, total_tokens, H, erase, recs);
+                           chunk_base, (int)n_seq, total_tokens, H, erase, recs, segs);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     e = record_mark(marks[1], stream);
     if (e != hipSuccess) return e;
-    if (use_column_split(n_seq * H))
+    if (L.scan.P > 0) {  // one sequence: its records are numbered by chunk, with or without offsets
+        const int P = L.scan.P;
+        int32_t *seg_cu = reinterpret_cast<int32_t *>(ws + L.seg_cu_off);
+        int32_t *seg_base = reinterpret_cast<int32_t *>(ws + L.seg_base_off);
+        const uint16_t *zero_page = reinterpret_cast<const uint16_t *>(ws + L.zero_off);
+        float *R = reinterpret_cast<float *>(ws + L.r_off), *M = reinterpret_cast<float *>(ws + L.m_off),
+              *Sin = reinterpret_cast<float *>(ws + L.sin_off);
+        // A1 (the segment offsets and the zero page were written by k_chunk_prep)
+        if (e == hipSuccess)
+            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, nullptr, o, R, recs, stream);
+        if (e == hipSuccess)  // A2
+            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, nullptr, o, M, recs, stream,
+                                zero_page);
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(k_scan_combine, dim3((unsigned)(64 * ((H + 7) / 8))), dim3(256), 0, stream, P, H,
+                               initial_state, R, M, Sin, final_state);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess)  // D (its final states land in R, no longer needed)
+            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, Sin, o, R, recs, stream);
+    } else if (use_column_split(n_seq * H))
         e = launch_chain_cs(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
                             final_state, recs, stream);
     else if (chain_waves(n_seq * H) == 4)

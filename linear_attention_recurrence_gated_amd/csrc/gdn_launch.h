@@ -27,12 +27,15 @@ hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k,
                                  const hipEvent_t *marks, hipStream_t stream);
 
 // Chunkwise-parallel prefill (64-token chunks, d = 128, bf16 q/k/v).
-size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H);
+// Chunked prefill modes: the library's choice, one chain per (sequence, head),
+// or the chunk-level scan (one sequence).
+enum { CHUNKED_AUTO = 0, CHUNKED_CHAIN = 1, CHUNKED_SCAN = 2 };
+size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H, int mode);
 hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v,
                                   const float *g, const float *beta, const int32_t *cu_seqlens,
                                   const int32_t *cu_seqlens_host, int64_t n_seq,
                                   int64_t total_tokens, int H, const float *initial_state,
-                                  float *o, float *final_state, void *workspace, int erase,
+                                  float *o, float *final_state, void *workspace, int erase, int mode,
                                   const hipEvent_t *marks, hipStream_t stream);
 
 // Pre-processing: conv (4 taps) + optional SiLU + L2 norm of q, k + gate maps,

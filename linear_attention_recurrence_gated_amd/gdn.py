@@ -25,7 +25,7 @@ GDN_BF16, GDN_FP32 = 0, 1
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 # variants (flags): the gated delta rule, no gate (g = 1), no erase term (linear-attention write)
 GDN_VARIANT_GATED_DELTA, GDN_VARIANT_NO_GATE, GDN_VARIANT_NO_ERASE = 0, 1, 2
-CHUNK_AUTO, CHUNK_SERIAL, CHUNK_64 = 0, 1, 64
+CHUNK_AUTO, CHUNK_SERIAL, CHUNK_64, CHUNK_64_CHAIN, CHUNK_64_SCAN = 0, 1, 64, 65, 66
 
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_SEQLENS", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_UNSUPPORTED", 8: "GDN_ERR_ALIAS",

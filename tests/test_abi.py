@@ -268,3 +268,17 @@ def test_decode_slots_host_checks():
         assert gdn.lib().gdn_status_string(10).decode() == "invalid state slots"
     st, _ = _decode_slots(B=0)
     assert st == 0  # nothing to do, nothing enqueued
+
+
+def test_scan_mode_validation():
+    # the scan takes one sequence of at least 128 tokens
+    cu = np.array([0, 100, 300], np.int32)
+    st, msg = _prefill(chunk=gdn.CHUNK_64_SCAN, dtype=gdn.GDN_BF16, dk=128, dv=128, cu=FAKE * 512,
+                       cu_host=_host(cu), n_seq=2, N=300)
+    assert st == 7, msg
+    st, msg = _prefill(chunk=gdn.CHUNK_64_SCAN, dtype=gdn.GDN_BF16, dk=128, dv=128, N=100)
+    assert st == 7, msg
+    assert gdn.prefill_algorithm(gdn.GDN_BF16, 128, 128, gdn.CHUNK_64_SCAN) == gdn.CHUNK_64_SCAN
+    assert gdn.prefill_algorithm(gdn.GDN_FP32, 128, 128, gdn.CHUNK_64_SCAN) == 0
+    assert gdn.prefill_workspace_bytes(4096, 1, 4, 128, 128, gdn.GDN_BF16, gdn.CHUNK_64_SCAN) > \
+        gdn.prefill_workspace_bytes(4096, 1, 4, 128, 128, gdn.GDN_BF16, gdn.CHUNK_64_CHAIN)
