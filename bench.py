@@ -48,10 +48,20 @@ PRE_BYTES_PER_TOKEN_HEAD = 2 * (3 * D * 2 + 2 * 4)                              
 PRE_BYTES_FIXED = 3 * H * D * 4 * 4 + 2 * 9 * H * D * 2                              # taps + conv state in/out
 
 
-def source_hash():
+# Sources each measured kernel is built from: its HBM byte counts (profiles/traffic.json)
+# stay valid while these files are unchanged.
+KERNEL_SOURCES = {
+    "k_chunk_prep": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h"),
+    "k_chunk_chain": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h"),
+    "k_decode_step": ("gdn_rowstream.hip", "gdn_device.h"),
+    "k_preprocess": ("gdn_preprocess.hip", "gdn_device.h"),
+}
+
+
+def source_hash(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_recurrence_gated_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -59,7 +69,7 @@ def source_hash():
 
 def load_traffic(kernel):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/), if the
-    kernel sources still match the build the counters were taken on."""
+    kernel's sources still match the build the counters were taken on."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -67,10 +77,10 @@ def load_traffic(kernel):
         data = json.load(open(path))
     except ValueError:
         return None
-    if data.get("source_hash") != source_hash():
-        return None
     entry = data.get("kernels", {}).get(kernel)
-    return None if entry is None else entry.get("bytes_per_launch")
+    if entry is None or entry.get("source_hash") != source_hash(kernel):
+        return None
+    return entry.get("bytes_per_launch")
 
 
 def run_conditions(torch):
