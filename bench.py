@@ -7,9 +7,11 @@ bandwidth (B = 64, H = 48, d = 128, 256 in-place steps) as GB/s and % of the HBM
 peak.  Inputs are seeded synthetic data already resident in HBM when timing
 starts.
 
-One timed step = gdn_state_init (zero the layer's state) + gdn_prefill over the
-4096-token batch.  The decode half is timed as one pass of 256 gdn_decode_step
-calls.  Timing uses HIP events recorded on the stream every kernel is launched
+One timed step = one gdn_prefill call over the 4096-token batch from a zero
+initial state (initial_state NULL: the kernels start from zeros), writing o
+and the final state.  The decode half is timed as one pass of 256
+gdn_decode_step calls.  Further entries time the pre-processing, the serving
+form of the decode step and the chunk-level scan.  Timing uses HIP events recorded on the stream every kernel is launched
 on (torch's current stream).  The CPU oracle (test infrastructure) is timed on
 the host's cores as a reported baseline.
 
@@ -115,14 +117,12 @@ def bench_prefill(torch, gdn, w, steps, warmup, rotate):
     ws = torch.empty(gdn.prefill_workspace_bytes(T, 1, H, D, D, gdn.GDN_BF16, gdn.CHUNK_64), dtype=torch.uint8,
                      device=dev)
 
-    def call(x):
-        gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], initial_state=x["state"], final_state=x["state"],
+    def call(x):  # S_0 = 0: no initial state (the kernels start from zeros)
+        gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], initial_state=None, final_state=x["state"],
                     out=x["o"], workspace=ws, chunk=gdn.CHUNK_64)
 
     def step(i):
-        x = sets[i % rotate]
-        gdn.state_init(x["state"])
-        call(x)
+        call(sets[i % rotate])
 
     for i in range(warmup):
         step(i)

@@ -322,12 +322,18 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
 
     __shared__ PrepSmem S;
 
+    // the gates first (wave 0), so that their scan overlaps the row copies
+    float gl = 1.f, bl = 0.f;
+    if (wave == 0) {
+        const int64_t off = (t0 + min(lane, n - 1)) * H + h;
+        gl = g ? g[off] : 1.f;  // no g: the ungated rule
+        bl = beta[off];
+    }
     // q, k rows of the chunk -> LDS row tiles (8 one-kilobyte copies per wave)
     dma_rows(S.KL, k + cbase, rs, n, lane, wave, 4);
     dma_rows(S.QT, q + cbase, rs, n, lane, wave, 4);
-    if (wave == 0) {  // gate prefix sums and the record's gate factors
-        const int64_t off = (t0 + min(lane, n - 1)) * H + h;
-        const float gl = g ? g[off] : 1.f, bl = beta[off];  // no g: the ungated rule
+    float f_eg = 0.f, f_bw = 0.f, f_egm1 = 0.f, f_egn = 0.f;  // the record's gate factors (wave 0)
+    if (wave == 0) {  // gate prefix sums
         const float lam = (lane < n && g) ? __logf(fmaxf(gl, FLT_MIN)) : 0.f;
         const float bt = lane < n ? bl : 0.f;
         const float G = wave_inclusive_scan(lam, lane);
@@ -335,16 +341,22 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
         const float G63 = __shfl(G, 63, 64);
         S.G[lane] = G;
         S.B[lane] = bt;
-        float *gate = reinterpret_cast<float *>(rec + REC_GATE);
-        gate[GATE_EG + lane] = __expf(G);
-        gate[GATE_BW + lane] = bt * __expf(G63 - G);
+        f_eg = __expf(G);
+        f_bw = bt * __expf(G63 - G);
         // without the erase term nothing is recalled from the entering state:
         // Y = V - 0 X = V, and L = 0 below makes T = I, so U = V
-        gate[GATE_EGM1 + lane] = !erase ? 0.f : lane > 0 ? __expf(Gm1) : 1.f;
-        if (lane == 63) gate[GATE_EGN] = __expf(G63);
+        f_egm1 = !erase ? 0.f : lane > 0 ? __expf(Gm1) : 1.f;
+        f_egn = __expf(G63);
     }
     wait_all_vmem();
     lds_barrier();
+    if (wave == 0) {  // stored after the barrier: nothing waits for these writes
+        float *gate = reinterpret_cast<float *>(rec + REC_GATE);
+        gate[GATE_EG + lane] = f_eg;
+        gate[GATE_BW + lane] = f_bw;
+        gate[GATE_EGM1 + lane] = f_egm1;
+        if (lane == 63) gate[GATE_EGN] = f_egn;
+    }
 
     // K K^T tiles (the 10 tiles on and below the diagonal; item i = wave + 4 j,
     // i < 10, kept in registers until k's tile may be overwritten) and the P
@@ -910,6 +922,19 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         const u32x4_t *Pl = reinterpret_cast<const u32x4_t *>(B.rec + REC_P_LO);
         const float *gate = reinterpret_cast<const float *>(B.rec + REC_GATE);
 
+        // T and this wave's P blocks, read first: their LDS latency then hides
+        // behind the partial products (the buffer is stable until A_{c+1})
+        u32x4_t tfh[T_BLOCKS], tfl[T_BLOCKS];
+#pragma unroll
+        for (int b = 0; b < T_BLOCKS; ++b) {
+            tfh[b] = Th[b * 64 + lane];
+            tfl[b] = Tl[b * 64 + lane];
+        }
+        const int pz = tblk(tz, 0);  // tile tz in {2, 3} has blocks pz, pz + 1; tile ta in {0, 1} is block ta
+        const u32x4_t pah = Ph[ta * 64 + lane], pal = Pl[ta * 64 + lane];
+        const u32x4_t pz0h = Ph[pz * 64 + lane], pz0l = Pl[pz * 64 + lane];
+        const u32x4_t pz1h = Ph[(pz + 1) * 64 + lane], pz1l = Pl[(pz + 1) * 64 + lane];
+
         // partial X = K S0^T and Q S0^T over this wave's 64 columns (k steps 2 hf, 2 hf + 1)
         u32x4_t bSh[2], bSl[2];
 #pragma unroll
@@ -958,7 +983,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             U[tb] = zero4();
 #pragma unroll
             for (int ks = 0; ks <= (tb >> 1); ++ks)
-                U[tb] = mfma3(Th[tblk(tb, ks) * 64 + lane], Tl[tblk(tb, ks) * 64 + lane], bYh[ks], bYl[ks], U[tb]);
+                U[tb] = mfma3(tfh[tblk(tb, ks)], tfl[tblk(tb, ks)], bYh[ks], bYl[ks], U[tb]);
         }
         // O = diag(e^{G_t}) Q S0^T + P U for this wave's two tiles
         u32x4_t bUh[2], bUl[2];
@@ -966,21 +991,25 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
         float *ob = o + t0 * rs + h * DK;
         const int ooff = 4 * g4 * rs + iw + r;
+        {
+            const f32x4_t Oa = hf ? O[1] : O[0], Oz = hf ? O[2] : O[3];  // tiles ta, tz (uniform selects)
+            f32x4_t acc[2];
+            acc[0] = Oa * *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * ta + 4 * g4);
+            acc[0] = mfma3(pah, pal, bUh[0], bUl[0], acc[0]);
+            acc[1] = Oz * *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * tz + 4 * g4);
+            acc[1] = mfma3(pz0h, pz0l, bUh[0], bUl[0], acc[1]);
+            acc[1] = mfma3(pz1h, pz1l, bUh[1], bUl[1], acc[1]);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            if (tb != ta && tb != tz) continue;  // uniform; keeps O[] indices static
-            f32x4_t acc = O[tb] * *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * tb + 4 * g4);
+            for (int x = 0; x < 2; ++x) {
+                const int tb = x ? tz : ta;
+                if (n == C) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                if (ks <= (tb >> 1))
-                    acc = mfma3(Ph[tblk(tb, ks) * 64 + lane], Pl[tblk(tb, ks) * 64 + lane], bUh[ks], bUl[ks], acc);
-            if (n == C) {
+                    for (int e = 0; e < 4; ++e) ob[ooff + (16 * tb + e) * rs] = acc[x][e];
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ob[ooff + (16 * tb + e) * rs] = acc[e];
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (16 * tb + 4 * g4 + e < n) ob[ooff + (16 * tb + e) * rs] = acc[e];
+                    for (int e = 0; e < 4; ++e)
+                        if (16 * tb + 4 * g4 + e < n) ob[ooff + (16 * tb + e) * rs] = acc[x][e];
+                }
             }
         }
 
