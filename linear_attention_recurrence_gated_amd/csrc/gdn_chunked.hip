@@ -811,7 +811,9 @@ __device__ __forceinline__ const uint32_t *chunk_line(const char *rec, const uin
 
 // vz: NULL, or a page of at least 64 zero bytes that stands in for every row
 // of v; the chain then runs the homogeneous part of the update (v = 0) from
-// S = I, and initial_state is not read.
+// S = I, and initial_state is not read.  OUTS = false: only the final states
+// are formed (no read-out products, no stores of o; o is not used).
+template <bool OUTS>
 __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ seq_order,
@@ -832,6 +834,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
     const int rs = H * DK;
     const int vcol0 = tile * 32;  // the workgroup's first row of S = first column of v
+    constexpr bool outs = OUTS;  // false: the state only (no read-out)
 
     __shared__ __attribute__((aligned(16))) ChainSmemCS sm;
 
@@ -931,9 +934,15 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             tfl[b] = Tl[b * 64 + lane];
         }
         const int pz = tblk(tz, 0);  // tile tz in {2, 3} has blocks pz, pz + 1; tile ta in {0, 1} is block ta
-        const u32x4_t pah = Ph[ta * 64 + lane], pal = Pl[ta * 64 + lane];
-        const u32x4_t pz0h = Ph[pz * 64 + lane], pz0l = Pl[pz * 64 + lane];
-        const u32x4_t pz1h = Ph[(pz + 1) * 64 + lane], pz1l = Pl[(pz + 1) * 64 + lane];
+        u32x4_t pah, pal, pz0h, pz0l, pz1h, pz1l;
+        if (outs) {
+            pah = Ph[ta * 64 + lane];
+            pal = Pl[ta * 64 + lane];
+            pz0h = Ph[pz * 64 + lane];
+            pz0l = Pl[pz * 64 + lane];
+            pz1h = Ph[(pz + 1) * 64 + lane];
+            pz1l = Pl[(pz + 1) * 64 + lane];
+        }
 
         // partial X = K S0^T and Q S0^T over this wave's 64 columns (k steps 2 hf, 2 hf + 1)
         u32x4_t bSh[2], bSl[2];
@@ -947,7 +956,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 X[tb] = mfma2b(rowfrag_slots(B.K, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], X[tb]);
-                O[tb] = mfma2b(rowfrag_slots(B.Q, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], O[tb]);
+                if (outs) O[tb] = mfma2b(rowfrag_slots(B.Q, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], O[tb]);
             }
             sm.xch[wave][tb][lane] = X[tb];
             sm.xch[wave][4 + tb][lane] = O[tb];
@@ -991,7 +1000,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
         float *ob = o + t0 * rs + h * DK;
         const int ooff = 4 * g4 * rs + iw + r;
-        {
+        if (outs) {
             const f32x4_t Oa = hf ? O[1] : O[0], Oz = hf ? O[2] : O[3];  // tiles ta, tz (uniform selects)
             f32x4_t acc[2];
             acc[0] = Oa * *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * ta + 4 * g4);
@@ -1040,7 +1049,8 @@ hipError_t launch_chain_cs(const void *q, const void *k, const void *v, const in
                            hipStream_t stream, const uint16_t *vz = nullptr) {
     const int64_t units = n_seq * H;
     const int64_t grid = ((units + 7) / 8) * 8 * CS_TILES;
-    hipLaunchKernelGGL(k_chunk_chain_cs, dim3((unsigned)grid), dim3(512), 0, stream,
+    auto kern = o ? k_chunk_chain_cs<true> : k_chunk_chain_cs<false>;  // o == NULL: final states only
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), cu, chunk_base, seq_order, (int)n_seq, total_tokens, H,
                        initial_state, o, final_state, recs, vz);
@@ -1074,18 +1084,18 @@ hipError_t launch_chain(const void *q, const void *k, const void *v, const int32
 //   D   every segment from S_in(j) with the real v     -> the outputs
 // The records of the per-chunk kernel serve all three passes unchanged.
 
-// combine: one 4-wave workgroup per (head, block of 16 state rows); the rows
-// of S are independent.  Wave w forms columns 32 w .. 32 w + 31 of
-// S_in(j) M_j + R_j on fp32 MFMA (v_mfma_f32_16x16x4f32: lane (g, r) holds
-// A[r][g] and B[g][r]; result rows 4 g + e of column r), as four independent
-// accumulator chains (two column tiles x two halves of k).  The M and R
-// values of step j + 1 are loaded while step j is formed.  The eight
-// workgroups of a head run on one XCD (block b runs on XCD b % 8) and touch
-// M and R of step j + 1 + SCAN_TOUCH ahead of use, each an eighth of M's
-// lines and its own rows of R, so that the loads hit in that XCD's L2.
+// combine: one 8-wave workgroup per (head, block of 16 state rows); the rows
+// of S are independent.  Wave w forms the 16 x 16 tile of columns
+// 16 w .. 16 w + 15 of S_in(j) M_j + R_j on bf16 MFMA with both operands split
+// (hi + lo, three products each, as in the chain) over four k steps of 32;
+// two waves per SIMD hide each other's latencies.  The M and R values of step
+// j + 1 are loaded while step j is formed.  The eight workgroups of a head run
+// on one XCD (block b runs on XCD b % 8) and touch M and R of step
+// j + 1 + SCAN_TOUCH ahead of use, each an eighth of M's lines and its own rows
+// of R, so that the loads hit in that XCD's L2.
 constexpr int SCAN_TOUCH = 3;
 
-__global__ __launch_bounds__(256) void k_scan_combine(int P, int H, const float *s0, const float *__restrict__ R,
+__global__ __launch_bounds__(512) void k_scan_combine(int P, int H, const float *s0, const float *__restrict__ R,
                                                       const float *__restrict__ M, float *__restrict__ s_in,
                                                       float *final_state) {
     const int bid = blockIdx.x;
@@ -1093,10 +1103,10 @@ __global__ __launch_bounds__(256) void k_scan_combine(int P, int H, const float 
     if (h >= H) return;
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int row0 = 16 * rb, c0 = 32 * wave;
+    const int row0 = 16 * rb, c0 = 16 * wave;
     const int64_t dd = (int64_t)DK * DK;
     __shared__ float Srow[16][DK + 4];
-    __shared__ __attribute__((aligned(16))) char scratch[4 * 1024];  // landing area of the line touches
+    __shared__ __attribute__((aligned(16))) char scratch[8 * 256];  // landing area of the line touches
 
     // lines of step j touched by this thread: tid < 64: line 8 tid + rb of M_j
     // (an eighth of its 512); 64 <= tid < 128: line tid - 64 of this block's
@@ -1106,26 +1116,24 @@ __global__ __launch_bounds__(256) void k_scan_combine(int P, int H, const float 
         const float *src = tid < 64            ? M + sh + (int64_t)(8 * tid + rb) * 32
                          : tid < 128           ? R + sh + (int64_t)row0 * DK + (int64_t)(tid - 64) * 32
                                                : M + sh + (int64_t)rb * 32;
-        __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)(scratch + wave * 1024), 4, 0,
+        __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)(scratch + wave * 256), 4, 0,
                                          0);
     };
     for (int j = 1; j <= SCAN_TOUCH && j < P; ++j) touch(j);
 
-    // lane (g, r) of tile t needs M[4 ks + g][c0 + 16 t + r], ks = 0..31, and
-    // R[row0 + 4 g + e][c0 + 16 t + r]
-    float mc[2][DK / 4], rc[2][4], mn[2][DK / 4], rn[2][4];
-    auto load = [&](int j, float (&m)[2][DK / 4], float (&rr)[2][4]) {
+    // lane (g, r), k step kb: M[32 kb + slot_k(g, e)][c0 + r], e = 0..7, and R[row0 + 4 g + e][c0 + r], e = 0..3
+    float mc[4][8], rc[4], mn[4][8], rn[4];
+    auto load = [&](int j, float (&m)[4][8], float (&rr)[4]) {
         const int64_t sh = ((int64_t)j * H + h) * dd;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int ks = 0; ks < DK / 4; ++ks) m[t][ks] = M[sh + (int64_t)(4 * ks + g4) * DK + c0 + 16 * t + r];
+            for (int e = 0; e < 8; ++e) m[kb][e] = M[sh + (int64_t)(32 * kb + slot_k(g4, e)) * DK + c0 + r];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rr[t][e] = R[sh + (int64_t)(row0 + 4 * g4 + e) * DK + c0 + 16 * t + r];
-        }
+        for (int e = 0; e < 4; ++e) rr[e] = R[sh + (int64_t)(row0 + 4 * g4 + e) * DK + c0 + r];
     };
     load(0, mc, rc);
-    for (int i = tid; i < 16 * DK; i += 256) {  // S_in(0) = S_0: read before anything is written
+    for (int i = tid; i < 16 * DK; i += 512) {  // S_in(0) = S_0: read before anything is written
         const int rr = i / DK, cc = i % DK;
         const float x = s0 ? s0[(int64_t)h * dd + (int64_t)(row0 + rr) * DK + cc] : 0.f;
         Srow[rr][cc] = x;
@@ -1135,40 +1143,32 @@ __global__ __launch_bounds__(256) void k_scan_combine(int P, int H, const float 
     for (int j = 0; j < P; ++j) {
         if (j + 1 < P) load(j + 1, mn, rn);
         if (j + 1 + SCAN_TOUCH < P) touch(j + 1 + SCAN_TOUCH);
-        f32x4_t acc[2][2];
+        f32x4_t acc = f32x4_t{rc[0], rc[1], rc[2], rc[3]};
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            acc[t][0] = f32x4_t{rc[t][0], rc[t][1], rc[t][2], rc[t][3]};
-            acc[t][1] = zero4();
-        }
+        for (int kb = 0; kb < 4; ++kb) {
+            float a[8];
 #pragma unroll
-        for (int ks = 0; ks < DK / 8; ++ks) {
-            const float a0 = Srow[r][4 * ks + g4], a1 = Srow[r][DK / 2 + 4 * ks + g4];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                acc[t][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, mc[t][ks], acc[t][0], 0, 0, 0);
-                acc[t][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, mc[t][DK / 8 + ks], acc[t][1], 0, 0, 0);
-            }
+            for (int e = 0; e < 8; ++e) a[e] = Srow[r][32 * kb + slot_k(g4, e)];
+            u32x4_t ah, al, bh, bl;
+            split8(a, ah, al);
+            split8(mc[kb], bh, bl);
+            acc = mfma3(ah, al, bh, bl, acc);
         }
         __syncthreads();  // every wave has read S_in(j)
         float *dst = j + 1 < P ? s_in + ((int64_t)(j + 1) * H + h) * dd : final_state + (int64_t)h * dd;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rr = 4 * g4 + e, cc = c0 + 16 * t + r;
-                const float x = acc[t][0][e] + acc[t][1][e];
-                Srow[rr][cc] = x;
-                dst[(int64_t)(row0 + rr) * DK + cc] = x;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int rr = 4 * g4 + e, cc = c0 + r;
+            Srow[rr][cc] = acc[e];
+            dst[(int64_t)(row0 + rr) * DK + cc] = acc[e];
+        }
         __syncthreads();
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int ks = 0; ks < DK / 4; ++ks) mc[t][ks] = mn[t][ks];
+            for (int e = 0; e < 8; ++e) mc[kb][e] = mn[kb][e];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rc[t][e] = rn[t][e];
-        }
+        for (int e = 0; e < 4; ++e) rc[e] = rn[e];
     }
 }
 
@@ -1257,13 +1257,14 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
         float *R = reinterpret_cast<float *>(ws + L.r_off), *M = reinterpret_cast<float *>(ws + L.m_off),
               *Sin = reinterpret_cast<float *>(ws + L.sin_off);
         // A1 (the segment offsets and the zero page were written by k_chunk_prep)
-        if (e == hipSuccess)
-            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, nullptr, o, R, recs, stream);
+        if (e == hipSuccess)  // (A1 and A2 form states only)
+            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, nullptr, nullptr, R, recs,
+                                stream);
         if (e == hipSuccess)  // A2
-            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, nullptr, o, M, recs, stream,
-                                zero_page);
+            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, nullptr, nullptr, M, recs,
+                                stream, zero_page);
         if (e == hipSuccess) {
-            hipLaunchKernelGGL(k_scan_combine, dim3((unsigned)(64 * ((H + 7) / 8))), dim3(256), 0, stream, P, H,
+            hipLaunchKernelGGL(k_scan_combine, dim3((unsigned)(64 * ((H + 7) / 8))), dim3(512), 0, stream, P, H,
                                initial_state, R, M, Sin, final_state);
             e = hipGetLastError();
         }
