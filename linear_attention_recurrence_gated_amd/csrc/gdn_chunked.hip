@@ -324,14 +324,15 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
 
     // the gates first (wave 0), so that their scan overlaps the row copies
     float gl = 1.f, bl = 0.f;
-    if (wave == 0) {
+    if (wave == 0) {  // unconditional loads (no g: beta's value stands in and is not used)
         const int64_t off = (t0 + min(lane, n - 1)) * H + h;
-        gl = g ? g[off] : 1.f;  // no g: the ungated rule
+        gl = (g ? g : beta)[off];
         bl = beta[off];
     }
     // q, k rows of the chunk -> LDS row tiles (8 one-kilobyte copies per wave)
     dma_rows(S.KL, k + cbase, rs, n, lane, wave, 4);
     dma_rows(S.QT, q + cbase, rs, n, lane, wave, 4);
+    asm volatile("" : "+v"(gl), "+v"(bl));  // keeps the gate arithmetic after the copies are issued
     float f_eg = 0.f, f_bw = 0.f, f_egm1 = 0.f, f_egn = 0.f;  // the record's gate factors (wave 0)
     if (wave == 0) {  // gate prefix sums
         const float lam = (lane < n && g) ? __logf(fmaxf(gl, FLT_MIN)) : 0.f;
