@@ -18,8 +18,9 @@
  *   - Pointers are DEVICE pointers unless the name ends in _host.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it; nothing synchronises and nothing allocates.
- *   - The caller owns every buffer.  The library keeps no device memory and no
- *     global state except a per-thread copy of the last error message.
+ *   - The caller owns every buffer.  The library keeps no device memory; its
+ *     only host state is per thread: the last error message and the events
+ *     armed by gdn_prefill_set_marks.
  *   - Arguments are validated on the host before anything is enqueued.  On any
  *     error the call returns a non-zero gdn_status, enqueues nothing and leaves
  *     every output untouched; gdn_last_error() then describes the problem.

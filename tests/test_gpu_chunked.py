@@ -125,6 +125,23 @@ def test_many_pairs_use_the_two_workgroup_chain(oracle_lib):
     check(inp, what="72 pairs")
 
 
+def test_thousands_of_short_sequences(oracle_lib):
+    """5,000 packed sequences of 0 to 9 tokens (more than the planner orders
+    by length), each with its own initial state."""
+    say("5000 short sequences")
+    lengths = np.random.default_rng(16).integers(0, 10, size=5000).tolist()
+    inp = w.make_prefill(lengths, H=2, d=128, seed=16, gate_shift=-1.0, init_std=0.2)
+    check(inp, what="5000 sequences")
+
+
+def test_sixty_four_heads_fill_the_column_split(oracle_lib):
+    """64 (sequence, head) pairs: the largest count that still takes the
+    column-split chain (four workgroups per pair, 256 in all)."""
+    say("64 heads, one sequence")
+    inp = w.make_prefill([700], H=64, d=128, seed=17, gate_shift=-1.0, init_std=0.2, packed=False)
+    check(inp, what="H=64")
+
+
 def _head_slice(inp, heads):
     """The same inputs restricted to some heads (for oracle runs on a sample)."""
     return w.PrefillInputs(np.ascontiguousarray(inp.q[:, heads]), np.ascontiguousarray(inp.k[:, heads]),
