@@ -394,8 +394,8 @@ gdn_status gdn_preprocess(const void *xq, const void *xk, const void *xv, gdn_dt
     if (conv_state_in && conv_state_in != conv_state_out && overlap(rso, Range{conv_state_in, sb}))
         return fail(GDN_ERR_ALIAS, "preprocess: conv_state_in partially overlaps conv_state_out");
     return hip_status(gdn::launch_preprocess(dtype == GDN_BF16, d, xq, xk, xv, conv_w, conv_state_in, conv_state_out,
-                                             a_logit, b_logit, gate_bias, cu_seqlens, n_seq, total_tokens, H,
-                                             activation, q, k, v, g, beta, (hipStream_t)stream),
+                                             a_logit, b_logit, gate_bias, cu_seqlens, cu_seqlens_host, n_seq,
+                                             total_tokens, H, activation, q, k, v, g, beta, (hipStream_t)stream),
                       "preprocess launch");
 }
 

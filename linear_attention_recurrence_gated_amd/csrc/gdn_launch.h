@@ -42,8 +42,9 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v,
 // then the returned conv state.
 hipError_t launch_preprocess(bool bf16, int d, const void *xq, const void *xk, const void *xv, const float *w,
                              const void *st_in, void *st_out, const float *a_logit, const float *b_logit,
-                             const float *bias, const int32_t *cu, int64_t n_seq, int64_t total_tokens, int H, int act,
-                             void *q, void *k, void *v, float *g, float *beta, hipStream_t stream);
+                             const float *bias, const int32_t *cu, const int32_t *cu_host, int64_t n_seq,
+                             int64_t total_tokens, int H, int act, void *q, void *k, void *v, float *g, float *beta,
+                             hipStream_t stream);
 
 // state[0 : n_floats] = init ? init : 0
 hipError_t launch_state_fill(float *state, const float *init, int64_t n_floats, hipStream_t stream);

@@ -27,6 +27,9 @@
 // a contiguous run of token ranges (neighbouring ranges share window rows in
 // that XCD's L2).  Batches of short sequences (decode steps) use R = 1.
 //
+// The returned conv state (the last three raw inputs of each sequence) is
+// written by k_preprocess itself, by the thread at the sequence's last token,
+// from its window, when that is safe (see fuse_conv_state); otherwise by
 // k_conv_state: one thread per (sequence, tensor, head, channel) copies the
 // sequence's last three raw inputs (shifting in the starting state for a
 // sequence shorter than three) to the returned conv state.  It reads all
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256) void k_preprocess(const TIn *__restrict__ xq, 
                                                     int n_seq, int64_t total_tokens, int H, int act, int n_hg,
                                                     uint32_t n_ranges, TIn *__restrict__ yq, TIn *__restrict__ yk,
                                                     TIn *__restrict__ yv, float *__restrict__ g,
-                                                    float *__restrict__ beta) {
+                                                    float *__restrict__ beta, TIn *st_out) {
     using V = Vec8<TIn>;
     constexpr int LPR = D / 8;      // lanes per head
     constexpr int HPB = 256 / LPR;  // heads per workgroup
@@ -156,6 +159,7 @@ __global__ __launch_bounds__(256) void k_preprocess(const TIn *__restrict__ xq, 
     const TIn *x = (tau == 0 ? xq : tau == 1 ? xk : xv) + col;
     TIn *y = (tau == 0 ? yq : tau == 1 ? yk : yv) + col;
     const TIn *st = st_in + col;  // used only when st_in is given (tested on st_in: uniform)
+    TIn *so = st_out + col;       // used only when st_out is given: the returned conv state
     const bool normalise = tau < 2;
 
     float tap[8][4];
@@ -197,6 +201,10 @@ __global__ __launch_bounds__(256) void k_preprocess(const TIn *__restrict__ xq, 
             pre_token<TIn, LPR>(tap, win[i], win[i + 1], win[i + 2], win[i + 3], act, normalise, hl,
                                 y + (ta + i) * rs);
         }
+        if (st_out && hl && ta + R == t1) {  // the sequence ends here: its last three raw inputs
+#pragma unroll
+            for (int j = 0; j < 3; ++j) V::store(so + ((int64_t)(s0 * 3 + tau) * 3 + j) * rs, win[R + j]);
+        }
     } else {
         // General path (a range holding a sequence start or the batch's end):
         // each token loads its own window.
@@ -221,6 +229,10 @@ __global__ __launch_bounds__(256) void k_preprocess(const TIn *__restrict__ xq, 
 #pragma unroll
             for (int j = 0; j < 4; ++j) V::unpack(raw[j], wv[j]);
             pre_token<TIn, LPR>(tap, wv[0], wv[1], wv[2], wv[3], act, normalise, hl, y + t * rs);
+            if (st_out && hl && t == q1 - 1) {  // the sequence ends here: its last three raw inputs
+#pragma unroll
+                for (int j = 0; j < 3; ++j) V::store(so + ((int64_t)(s * 3 + tau) * 3 + j) * rs, wv[j + 1]);
+            }
         }
     }
 
@@ -270,7 +282,7 @@ template <typename TIn, int D, int R>
 hipError_t launch_pre_kernel(const void *xq, const void *xk, const void *xv, const float *w, const void *st_in,
                              const float *a, const float *b, const float *bias, const int32_t *cu, int64_t n_seq,
                              int64_t N, int H, int act, void *q, void *k, void *v, float *g, float *beta,
-                             hipStream_t stream) {
+                             void *st_out_fused, hipStream_t stream) {
     constexpr int HPB = 256 / (D / 8);
     const int n_hg = (H + HPB - 1) / HPB;
     const int64_t n_ranges = (N + R - 1) / R;
@@ -278,32 +290,48 @@ hipError_t launch_pre_kernel(const void *xq, const void *xk, const void *xv, con
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_preprocess<TIn, D, R>), dim3((unsigned)blocks), dim3(256), 0, stream, (const TIn *)xq,
                        (const TIn *)xk, (const TIn *)xv, w, (const TIn *)st_in, a, b, bias, cu, (int)n_seq, N, H, act,
-                       n_hg, (uint32_t)n_ranges, (TIn *)q, (TIn *)k, (TIn *)v, g, beta);
+                       n_hg, (uint32_t)n_ranges, (TIn *)q, (TIn *)k, (TIn *)v, g, beta, (TIn *)st_out_fused);
     return hipGetLastError();
+}
+
+// Whether k_preprocess can return the conv state itself (the thread at each
+// sequence's last token writes it) instead of k_conv_state: not when a
+// sequence is empty (nothing runs for it), and, when the state is updated in
+// place, only if every sequence lies in one range of R tokens (its first
+// range reads the state in the same thread that writes it).
+bool fuse_conv_state(const int32_t *cu_host, int64_t n_seq, int64_t N, int R, bool in_place) {
+    for (int64_t s = 0; s < n_seq; ++s) {
+        const int64_t t0 = cu_host ? cu_host[s] : 0, t1 = cu_host ? cu_host[s + 1] : N;
+        if (t1 == t0) return false;
+        if (in_place && t0 / R != (t1 - 1) / R) return false;
+    }
+    return true;
 }
 
 template <typename TIn, int D>
 hipError_t preprocess_d(const void *xq, const void *xk, const void *xv, const float *w, const void *st_in,
                         void *st_out, const float *a, const float *b, const float *bias, const int32_t *cu,
-                        int64_t n_seq, int64_t N, int H, int act, void *q, void *k, void *v, float *g, float *beta,
-                        hipStream_t stream) {
+                        const int32_t *cu_host, int64_t n_seq, int64_t N, int H, int act, void *q, void *k, void *v,
+                        float *g, float *beta, hipStream_t stream) {
 #ifndef GDN_PRE_RANGE_BF16
 #define GDN_PRE_RANGE_BF16 16
 #endif
     // tokens per range: 16 rows of bf16 or 8 of fp32, 64 VGPRs in flight either way
     constexpr int R_LONG = sizeof(TIn) == 2 ? GDN_PRE_RANGE_BF16 : 8;
+    // ranges of R_LONG tokens pay off when sequences are longer than a range
+    const bool long_seqs = N >= (int64_t)R_LONG * n_seq;
+    const bool fused = N > 0 && fuse_conv_state(cu_host, n_seq, N, long_seqs ? R_LONG : 1, st_in && st_in == st_out);
     if (N > 0) {
-        // ranges of R_LONG tokens pay off when sequences are longer than a range
-        const bool long_seqs = N >= (int64_t)R_LONG * n_seq;
+        void *so = fused ? st_out : nullptr;
         const hipError_t e =
             long_seqs ? launch_pre_kernel<TIn, D, R_LONG>(xq, xk, xv, w, st_in, a, b, bias, cu, n_seq, N, H, act, q, k,
-                                                          v, g, beta, stream)
+                                                          v, g, beta, so, stream)
                       : launch_pre_kernel<TIn, D, 1>(xq, xk, xv, w, st_in, a, b, bias, cu, n_seq, N, H, act, q, k, v,
-                                                     g, beta, stream);
+                                                     g, beta, so, stream);
         if (e != hipSuccess) return e;
     }
     const int64_t n = n_seq * 3LL * H * D;
-    if (n > 0) {
+    if (n > 0 && !fused) {
         hipLaunchKernelGGL((k_conv_state<TIn>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                            (const TIn *)xq, (const TIn *)xk, (const TIn *)xv, (const TIn *)st_in, (TIn *)st_out, cu,
                            n_seq, N, H, D);
@@ -316,14 +344,15 @@ hipError_t preprocess_d(const void *xq, const void *xk, const void *xv, const fl
 
 hipError_t launch_preprocess(bool bf16, int d, const void *xq, const void *xk, const void *xv, const float *w,
                              const void *st_in, void *st_out, const float *a_logit, const float *b_logit,
-                             const float *bias, const int32_t *cu, int64_t n_seq, int64_t total_tokens, int H, int act,
-                             void *q, void *k, void *v, float *g, float *beta, hipStream_t stream) {
+                             const float *bias, const int32_t *cu, const int32_t *cu_host, int64_t n_seq,
+                             int64_t total_tokens, int H, int act, void *q, void *k, void *v, float *g, float *beta,
+                             hipStream_t stream) {
 #define GDN_PRE(D)                                                                                              \
     case D:                                                                                                     \
-        return bf16 ? preprocess_d<uint16_t, D>(xq, xk, xv, w, st_in, st_out, a_logit, b_logit, bias, cu, n_seq, \
-                                                total_tokens, H, act, q, k, v, g, beta, stream)                 \
-                    : preprocess_d<float, D>(xq, xk, xv, w, st_in, st_out, a_logit, b_logit, bias, cu, n_seq,    \
-                                             total_tokens, H, act, q, k, v, g, beta, stream);
+        return bf16 ? preprocess_d<uint16_t, D>(xq, xk, xv, w, st_in, st_out, a_logit, b_logit, bias, cu,       \
+                                                cu_host, n_seq, total_tokens, H, act, q, k, v, g, beta, stream) \
+                    : preprocess_d<float, D>(xq, xk, xv, w, st_in, st_out, a_logit, b_logit, bias, cu, cu_host,  \
+                                             n_seq, total_tokens, H, act, q, k, v, g, beta, stream);
     switch (d) {
         GDN_PRE(16)
         GDN_PRE(32)

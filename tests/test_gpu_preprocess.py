@@ -121,6 +121,20 @@ def test_state_updated_in_place(oracle_lib):
     compare(inp, res, run_oracle(inp), "in place")
 
 
+@pytest.mark.parametrize("in_place", [False, True])
+def test_short_sequences_across_ranges(oracle_lib, in_place):
+    """No empty sequence, short ones crossing 16-token range boundaries: the
+    returned conv state is written by the pre-processing kernel itself (new
+    buffer) or, in place, by the separate pass."""
+    lengths = [1, 2, 70, 3, 1, 40, 2]  # 119 tokens: ranges of 16 (at least 16 per sequence on average)
+    say("preprocess short sequences, in place" if in_place else "preprocess short sequences")
+    inp = w.make_preprocess(lengths, H=3, d=64, dtype="bf16", seed=9, activation="silu")
+    d = to_dev(inp)
+    st = d["conv_state_in"]
+    res = run_gpu(inp, conv_state_in=st, conv_state_out=st if in_place else None)
+    compare(inp, res, run_oracle(inp), "in place" if in_place else "new buffer")
+
+
 def test_parts_equal_one_shot(oracle_lib):
     """Feeding each part's returned conv state to the next part gives the
     one-shot result bit for bit (the same kernel arithmetic either way)."""
