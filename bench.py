@@ -357,7 +357,8 @@ def pre_entry(pre_ms):
     ms = mean(pre_ms)
     gbs = nbytes / (ms / 1e3) / 1e9
     return {"mean_ms": ms, "p50_ms": pct(pre_ms, 50), "tokens_per_s_layer": T / (ms / 1e3),
-            "roofline": {"kernel": "k_preprocess + k_conv_state (one gdn_preprocess call)", "bound": "hbm",
+            "roofline": {"kernel": "k_preprocess (one gdn_preprocess call; it returns the conv state itself)",
+                         "bound": "hbm",
                          "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "algorithmic_bytes": nbytes, "traffic": load_traffic("k_preprocess")}}
 
