@@ -64,10 +64,11 @@ typedef enum {
 #define GDN_CHUNK_64 64      /* chunkwise-parallel, 64-token chunks, MFMA (bf16 q/k/v, d = 128);
                                 the library picks one of the two forms below */
 #define GDN_CHUNK_64_CHAIN 65 /* chunked; each (sequence, head) carries its state chunk to chunk */
-#define GDN_CHUNK_64_SCAN 66  /* chunked; one sequence cut into segments whose affine state maps
+#define GDN_CHUNK_64_SCAN 66  /* chunked; each sequence cut into segments whose affine state maps
                                  (S_out = S_in M + R) are formed in parallel and combined in order
                                  (the chunk-parallel state accumulation of "Qwen3.8-27B 架构深读",
-                                 section 三); picked by GDN_CHUNK_64 for one sequence with few heads */
+                                 section 三); picked by GDN_CHUNK_64 for few (sequence, head) pairs
+                                 when it is expected to be faster */
 
 /* Variants of the recurrence (the `variant` argument of gdn_prefill,
  * gdn_decode_step and gdn_decode_step_slots), from the equations of the
@@ -130,7 +131,7 @@ size_t gdn_prefill_workspace_bytes(int64_t total_tokens, int64_t n_seq, int32_t 
  *   o             [N][H][dv]  fp32 output (must not overlap any input)
  *   final_state   [n_seq][H][dv][dk] fp32 output
  *   chunk         GDN_CHUNK_AUTO, GDN_CHUNK_SERIAL, GDN_CHUNK_64, GDN_CHUNK_64_CHAIN or
- *                 GDN_CHUNK_64_SCAN (one sequence of >= 128 tokens, else GDN_ERR_UNSUPPORTED)
+ *                 GDN_CHUNK_64_SCAN (1 to 64 sequences and at least one token, else GDN_ERR_UNSUPPORTED)
  *   workspace     device scratch of at least gdn_prefill_workspace_bytes();
  *                 may be NULL when that is 0.  Its contents on entry do not matter.
  *   variant       GDN_VARIANT_* flags (0: the gated delta rule)

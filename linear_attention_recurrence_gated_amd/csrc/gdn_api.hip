@@ -245,8 +245,8 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
 
     hipStream_t st = (hipStream_t)stream;
     if (n_seq == 0) return ok();
-    if (algo == GDN_CHUNK_64_SCAN && (n_seq != 1 || total_tokens < 2 * 64))
-        return fail(GDN_ERR_UNSUPPORTED, "prefill: the chunk-level scan takes one sequence of at least 128 tokens");
+    if (algo == GDN_CHUNK_64_SCAN && !gdn::prefill_chunked_scan_supported(n_seq, total_tokens))
+        return fail(GDN_ERR_UNSUPPORTED, "prefill: the chunk-level scan takes 1 to 64 sequences and at least one token");
     if (is_chunked(algo)) {
         const size_t need = gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H, chunked_mode(algo));
         if (need > 0 && (!workspace || workspace_bytes < need))

@@ -39,7 +39,7 @@
 //                  head never exchange data.
 //   k_chunk_chain_cs  the same with four workgroups per (sequence, head) and
 //                  the columns of S split over pairs of waves, for few pairs.
-//   k_scan_combine the chunk-level scan for one sequence with few heads
+//   k_scan_combine the chunk-level scan for few (sequence, head) pairs
 //                  (three k_chunk_chain_cs passes over segments, then a short
 //                  ordered combine of their affine maps); see below.
 //
@@ -87,33 +87,102 @@ static_assert(REC_BYTES % 256 == 0, "record layout");
 
 constexpr int TILE = C * DK * 2;  // one bf16 row tile: 16 KiB
 
-// The chunk-level scan (one sequence, few heads): the sequence is cut into P
-// segments of cps chunks each (the last one possibly shorter).
+// The chunk-level scan (few (sequence, head) pairs): each sequence is cut
+// into segments of cps chunks (its last one possibly shorter); P segments in
+// all, at most SCAN_MAX_SEGMENTS.
+constexpr int SCAN_MAX_SEGMENTS = 64;
+
 struct ScanPlan {
     int P = 0, cps = 0;
+    int32_t cu[SCAN_MAX_SEGMENTS + 1];    // token offset of each segment (cu[P] = total tokens)
+    int32_t base[SCAN_MAX_SEGMENTS + 1];  // global chunk index of each segment's first chunk
+    int32_t seg0[SCAN_MAX_SEGMENTS + 1];  // first segment of each sequence (n_seq + 1 entries)
 };
 
-constexpr int SCAN_MIN_SEGMENTS = 6;  // below this the three chain passes cost more than one chain
+// Segments whose column-split passes fill the 256 CUs once (four workgroups
+// per (segment, head)), at least 2.
+int scan_budget(int H) { return std::max(2, 256 / (4 * H)); }
 
-ScanPlan scan_plan(int64_t total_tokens, int H, bool forced) {
-    ScanPlan sp;
-    const int64_t nc = (total_tokens + C - 1) / C;
-    const int64_t fit = 256 / ((int64_t)H * 4);  // segments whose column-split chains fill the CUs once
-    int64_t P = std::min<int64_t>(nc / 2, fit);
-    if (forced && nc >= 2) P = std::max<int64_t>(P, 2);
-    if (P < 2) return sp;
-    sp.cps = (int)((nc + P - 1) / P);
-    sp.P = (int)((nc + sp.cps - 1) / sp.cps);
-    return sp;
+// Segments the workspace holds room for.
+int scan_capacity(int64_t n_seq, int H) {
+    return (int)std::min<int64_t>(SCAN_MAX_SEGMENTS, std::max<int64_t>(scan_budget(H), n_seq));
+}
+
+// Whether the workspace reserves room for the scan: asked for, or possibly
+// chosen (a budget of at least four segments, no more sequences than that).
+bool scan_possible(int mode, int64_t n_seq, int H) {
+    if (mode == CHUNKED_CHAIN || n_seq > SCAN_MAX_SEGMENTS) return false;
+    return mode == CHUNKED_SCAN || (scan_budget(H) >= 4 && n_seq <= scan_budget(H));
+}
+
+// Plan the segments from the host copy of the offsets (NULL: one sequence).
+// The segment length cps is the one that minimises the estimated time, in
+// units of one chunk of the column-split chain (about 2.1 us, measured): the
+// three passes over cps chunks (2.75 together), a combine step (0.85) per
+// segment of the most-cut sequence, and 8.5 of fixed cost, against the chain's
+// max_s chunks_s.  Returns false when there is nothing to cut, more non-empty
+// sequences than segments fit, or (unless forced) no expected gain of 15%.
+// Segments fit: the budget (the passes fill the CUs once), or when forced
+// the workspace's capacity.
+bool plan_scan(const int32_t *cu_host, int64_t n_seq, int64_t N, int H, bool forced, ScanPlan &sp) {
+    sp.P = 0;
+    if (n_seq < 1 || n_seq > SCAN_MAX_SEGMENTS || (!forced && !scan_possible(CHUNKED_AUTO, n_seq, H))) return false;
+    auto chunks = [&](int64_t s) { return ((cu_host ? cu_host[s + 1] - cu_host[s] : N) + C - 1) / C; };
+    int64_t nc_max = 0, ne = 0;
+    for (int64_t s = 0; s < n_seq; ++s) {
+        nc_max = std::max(nc_max, chunks(s));
+        ne += chunks(s) > 0;
+    }
+    const int64_t target = forced ? scan_capacity(n_seq, H) : scan_budget(H);
+    if (nc_max == 0 || ne > target) return false;
+    double best = 1e30;
+    int64_t best_cps = 0;
+    // the longest sequence alone needs cps >= nc_max / target; past the first
+    // feasible cps the cost grows by at least 2.75 - 0.85 per step
+    for (int64_t cps = std::max<int64_t>(1, (nc_max + target - 1) / target); cps <= nc_max; ++cps) {
+        if (2.75 * (double)cps + 0.85 + 8.5 >= best) break;
+        int64_t P = 0, pmax = 0;
+        for (int64_t s = 0; s < n_seq; ++s) {
+            const int64_t ps = (chunks(s) + cps - 1) / cps;
+            P += ps;
+            pmax = std::max(pmax, ps);
+        }
+        if (P > target) continue;
+        const double cost = 2.75 * (double)cps + 0.85 * (double)pmax + 8.5;
+        if (cost < best) {
+            best = cost;
+            best_cps = cps;
+        }
+    }
+    if (best_cps == 0 || (!forced && best >= 0.85 * (double)nc_max)) return false;
+    sp.cps = (int)best_cps;
+    int P = 0;
+    int64_t cb = 0;  // chunks of the earlier sequences
+    for (int64_t s = 0; s < n_seq; ++s) {
+        const int64_t t0 = cu_host ? cu_host[s] : 0;
+        const int64_t nc = chunks(s);
+        sp.seg0[s] = P;
+        for (int64_t c = 0; c < nc; c += best_cps) {
+            sp.cu[P] = (int32_t)(t0 + c * C);
+            sp.base[P] = (int32_t)(cb + c);
+            ++P;
+        }
+        cb += nc;
+    }
+    sp.seg0[n_seq] = P;
+    sp.cu[P] = (int32_t)N;
+    sp.base[P] = (int32_t)cb;
+    sp.P = P;
+    return true;
 }
 
 struct WsLayout {
     size_t base_off, order_off, rec_off, total;
-    ScanPlan scan;                                                   // scan.P == 0: no scan
-    size_t seg_cu_off, seg_base_off, zero_off, r_off, m_off, sin_off;
+    int scan_cap = 0;  // segments the scan's area holds (0: no scan area)
+    size_t seg_cu_off, seg_base_off, seg0_off, zero_off, r_off, m_off, sin_off;
 };
 
-WsLayout ws_layout(int64_t total_tokens, int64_t n_seq, int H, int scan) {  // scan: 0 no, 1 chosen, 2 forced
+WsLayout ws_layout(int64_t total_tokens, int64_t n_seq, int H, bool scan_area) {
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     WsLayout L;
     L.base_off = 0;
@@ -121,12 +190,13 @@ WsLayout ws_layout(int64_t total_tokens, int64_t n_seq, int H, int scan) {  // s
     L.rec_off = L.order_off + up((size_t)n_seq * 4);
     const size_t max_chunks = (size_t)((total_tokens + C - 1) / C + n_seq);
     L.total = L.rec_off + max_chunks * (size_t)H * REC_BYTES;
-    if (scan) {
-        L.scan = scan_plan(total_tokens, H, scan == 2);
-        const size_t P = (size_t)L.scan.P, states = up(P * H * DK * DK * sizeof(float));
+    if (scan_area) {
+        L.scan_cap = scan_capacity(n_seq, H);
+        const size_t P = (size_t)L.scan_cap, states = up(P * H * DK * DK * sizeof(float));
         L.seg_cu_off = L.total;
-        L.seg_base_off = L.seg_cu_off + up((P + 1) * 4);
-        L.zero_off = L.seg_base_off + up((P + 1) * 4);
+        L.seg_base_off = L.seg_cu_off + up((SCAN_MAX_SEGMENTS + 1) * 4);
+        L.seg0_off = L.seg_base_off + up((SCAN_MAX_SEGMENTS + 1) * 4);
+        L.zero_off = L.seg0_off + up((SCAN_MAX_SEGMENTS + 1) * 4);
         L.r_off = L.zero_off + 256;
         L.m_off = L.r_off + states;
         L.sin_off = L.m_off + states;
@@ -287,13 +357,14 @@ __device__ __forceinline__ float4 t4(const char *qt, int t, int s4) {  // T[t][s
     return *reinterpret_cast<const float4 *>(qt + t * 256 + ((((s4 >> 2) ^ (t & 15)) << 4)));
 }
 
-// Segments of the chunk-level scan (cu == NULL: no scan): token and chunk
-// offsets of P segments of cps chunks, and a zero page; written by the first
-// workgroup of k_chunk_prep.
+// Segments of the chunk-level scan (cu == NULL: no scan): the plan's token
+// and chunk offsets and first segment per sequence, and a zero page; written
+// to the workspace by the first workgroup of k_chunk_prep.
 struct ScanSegs {
-    int32_t *cu = nullptr, *base = nullptr;
+    int32_t *cu = nullptr, *base = nullptr, *seg0 = nullptr;
     uint32_t *zero_page = nullptr;
-    int P = 0, cps = 0;
+    int P = 0, n_seq = 0;
+    int32_t h_cu[SCAN_MAX_SEGMENTS + 1], h_base[SCAN_MAX_SEGMENTS + 1], h_seg0[SCAN_MAX_SEGMENTS + 1];
 };
 
 __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -304,9 +375,10 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
                                                     char *__restrict__ recs, ScanSegs segs) {
     if (blockIdx.x == 0 && segs.cu) {
         for (int i = threadIdx.x; i <= segs.P; i += 256) {
-            segs.cu[i] = (int32_t)min((int64_t)i * segs.cps * C, total_tokens);
-            segs.base[i] = (int32_t)(i * segs.cps);
+            segs.cu[i] = segs.h_cu[i];
+            segs.base[i] = segs.h_base[i];
         }
+        for (int i = threadIdx.x; i <= segs.n_seq; i += 256) segs.seg0[i] = segs.h_seg0[i];
         if (threadIdx.x < 64) segs.zero_page[threadIdx.x] = 0u;
     }
     const int64_t gc = blockIdx.x / H;
@@ -1074,38 +1146,53 @@ hipError_t launch_chain(const void *q, const void *k, const void *v, const int32
 }
 
 // ---------------------------------------------------------------------------
-// Chunk-level scan for one sequence with few heads.  Over a segment of chunks
+// Chunk-level scan for few (sequence, head) pairs.  Over a segment of chunks
 // the state update is affine, S_out = S_in M + R ([GDN]'s recurrence is linear
 // in S with transitions g I - beta k k^T acting from the right).  Three
 // column-split chain passes over all segments at once, and a short sequential
 // combine:
 //   A1  every segment from S = 0 with the real v       -> R_j (its final state)
 //   A2  every segment from S = I with v = 0            -> M_j (the product of its transitions)
-//   combine  S_in(0) = S_0,  S_in(j+1) = S_in(j) M_j + R_j,  final state = S_in(P)
+//   combine  per sequence over its segments j0 .. j0 + P_s - 1:
+//            S_in(j0) = S_0,  S_in(j+1) = S_in(j) M_j + R_j,  final state = S_in(j0 + P_s)
 //   D   every segment from S_in(j) with the real v     -> the outputs
 // The records of the per-chunk kernel serve all three passes unchanged.
 
-// combine: one 8-wave workgroup per (head, block of 16 state rows); the rows
-// of S are independent.  Wave w forms the 16 x 16 tile of columns
+// combine: one 8-wave workgroup per (sequence, head, block of 16 state rows);
+// the rows of S are independent.  Wave w forms the 16 x 16 tile of columns
 // 16 w .. 16 w + 15 of S_in(j) M_j + R_j on bf16 MFMA with both operands split
 // (hi + lo, three products each, as in the chain) over four k steps of 32;
 // two waves per SIMD hide each other's latencies.  The M and R values of step
-// j + 1 are loaded while step j is formed.  The eight workgroups of a head run
-// on one XCD (block b runs on XCD b % 8) and touch M and R of step
+// j + 1 are loaded while step j is formed.  The eight workgroups of a
+// (sequence, head) pair run on one XCD (block b runs on XCD b % 8) and touch M
+// and R of step
 // j + 1 + SCAN_TOUCH ahead of use, each an eighth of M's lines and its own rows
 // of R, so that the loads hit in that XCD's L2.
 constexpr int SCAN_TOUCH = 3;
 
-__global__ __launch_bounds__(512) void k_scan_combine(int P, int H, const float *s0, const float *__restrict__ R,
+__global__ __launch_bounds__(512) void k_scan_combine(int n_seq, int H, const int32_t *__restrict__ seg0,
+                                                      const float *s0, const float *__restrict__ R,
                                                       const float *__restrict__ M, float *__restrict__ s_in,
                                                       float *final_state) {
     const int bid = blockIdx.x;
-    const int h = (bid & 7) + 8 * (bid >> 6), rb = (bid >> 3) & 7;  // grid: 64 per group of 8 heads
-    if (h >= H) return;
+    const int u = (bid & 7) + 8 * (bid >> 6), rb = (bid >> 3) & 7;  // grid: 64 per group of 8 pairs
+    if (u >= n_seq * H) return;
+    const int sq = u / H, h = u % H;
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int row0 = 16 * rb, c0 = 16 * wave;
-    const int64_t dd = (int64_t)DK * DK;
+    const int64_t dd = (int64_t)DK * DK, own = (int64_t)u * dd;  // this pair's initial and final state
+    const int j0 = seg0[sq], P = seg0[sq + 1] - j0;               // its segments
+    if (P == 0) {  // an empty sequence leaves its state as it came in
+        for (int i = tid; i < 16 * DK; i += 512) {
+            const int64_t at = own + (int64_t)row0 * DK + i;
+            final_state[at] = s0 ? s0[at] : 0.f;
+        }
+        return;
+    }
+    R += (int64_t)j0 * H * dd;
+    M += (int64_t)j0 * H * dd;
+    s_in += (int64_t)j0 * H * dd;
     __shared__ float Srow[16][DK + 4];
     __shared__ __attribute__((aligned(16))) char scratch[8 * 256];  // landing area of the line touches
 
@@ -1136,7 +1223,7 @@ __global__ __launch_bounds__(512) void k_scan_combine(int P, int H, const float 
     load(0, mc, rc);
     for (int i = tid; i < 16 * DK; i += 512) {  // S_in(0) = S_0: read before anything is written
         const int rr = i / DK, cc = i % DK;
-        const float x = s0 ? s0[(int64_t)h * dd + (int64_t)(row0 + rr) * DK + cc] : 0.f;
+        const float x = s0 ? s0[own + (int64_t)(row0 + rr) * DK + cc] : 0.f;
         Srow[rr][cc] = x;
         s_in[(int64_t)h * dd + (int64_t)(row0 + rr) * DK + cc] = x;
     }
@@ -1156,7 +1243,7 @@ __global__ __launch_bounds__(512) void k_scan_combine(int P, int H, const float 
             acc = mfma3(ah, al, bh, bl, acc);
         }
         __syncthreads();  // every wave has read S_in(j)
-        float *dst = j + 1 < P ? s_in + ((int64_t)(j + 1) * H + h) * dd : final_state + (int64_t)h * dd;
+        float *dst = j + 1 < P ? s_in + ((int64_t)(j + 1) * H + h) * dd : final_state + own;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int rr = 4 * g4 + e, cc = c0 + r;
@@ -1201,15 +1288,12 @@ bool use_column_split(int64_t units) {
 
 }  // namespace
 
-// 0: one chain per (sequence, head); 1: the scan, chosen; 2: the scan, asked for.
-int scan_chosen(int mode, int64_t n_seq, int64_t total_tokens, int H) {
-    if (mode == CHUNKED_SCAN) return 2;
-    if (mode == CHUNKED_CHAIN || n_seq != 1) return 0;
-    return scan_plan(total_tokens, H, false).P >= SCAN_MIN_SEGMENTS ? 1 : 0;
+size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H, int mode) {
+    return ws_layout(total_tokens, n_seq, H, scan_possible(mode, n_seq, H)).total;
 }
 
-size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H, int mode) {
-    return ws_layout(total_tokens, n_seq, H, scan_chosen(mode, n_seq, total_tokens, H)).total;
+bool prefill_chunked_scan_supported(int64_t n_seq, int64_t total_tokens) {
+    return n_seq >= 1 && n_seq <= SCAN_MAX_SEGMENTS && total_tokens > 0;
 }
 
 hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, const float *g, const float *beta,
@@ -1217,7 +1301,12 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
                                   int64_t total_tokens, int H, const float *initial_state, float *o,
                                   float *final_state, void *workspace, int erase, int mode,
                                   const hipEvent_t *marks, hipStream_t stream) {
-    const WsLayout L = ws_layout(total_tokens, n_seq, H, scan_chosen(mode, n_seq, total_tokens, H));
+    const WsLayout L = ws_layout(total_tokens, n_seq, H, scan_possible(mode, n_seq, H));
+    ScanPlan sp;
+    if (L.scan_cap > 0 && plan_scan(cu_seqlens_host, n_seq, total_tokens, H, mode == CHUNKED_SCAN, sp) &&
+        sp.P > L.scan_cap)
+        return hipErrorInvalidValue;  // (the plan never exceeds the room reserved for it)
+    if (mode == CHUNKED_SCAN && sp.P == 0) return hipErrorInvalidValue;  // (excluded by the caller's checks)
     hipError_t e = record_mark(marks[0], stream);
     if (e != hipSuccess) return e;
     char *ws = static_cast<char *>(workspace);
@@ -1234,12 +1323,16 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
         n_chunks = (total_tokens + C - 1) / C;
     }
     ScanSegs segs;
-    if (L.scan.P > 0) {
+    if (sp.P > 0) {
         segs.cu = reinterpret_cast<int32_t *>(ws + L.seg_cu_off);
         segs.base = reinterpret_cast<int32_t *>(ws + L.seg_base_off);
+        segs.seg0 = reinterpret_cast<int32_t *>(ws + L.seg0_off);
         segs.zero_page = reinterpret_cast<uint32_t *>(ws + L.zero_off);
-        segs.P = L.scan.P;
-        segs.cps = L.scan.cps;
+        segs.P = sp.P;
+        segs.n_seq = (int)n_seq;
+        std::copy(sp.cu, sp.cu + sp.P + 1, segs.h_cu);
+        std::copy(sp.base, sp.base + sp.P + 1, segs.h_base);
+        std::copy(sp.seg0, sp.seg0 + n_seq + 1, segs.h_seg0);
     }
     if (n_chunks > 0) {
         hipLaunchKernelGGL(k_chunk_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream,
@@ -1250,10 +1343,11 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     }
     e = record_mark(marks[1], stream);
     if (e != hipSuccess) return e;
-    if (L.scan.P > 0) {  // one sequence: its records are numbered by chunk, with or without offsets
-        const int P = L.scan.P;
+    if (sp.P > 0) {  // segments index the records as the sequences' chunks do
+        const int P = sp.P;
         int32_t *seg_cu = reinterpret_cast<int32_t *>(ws + L.seg_cu_off);
         int32_t *seg_base = reinterpret_cast<int32_t *>(ws + L.seg_base_off);
+        const int32_t *seg0 = reinterpret_cast<const int32_t *>(ws + L.seg0_off);
         const uint16_t *zero_page = reinterpret_cast<const uint16_t *>(ws + L.zero_off);
         float *R = reinterpret_cast<float *>(ws + L.r_off), *M = reinterpret_cast<float *>(ws + L.m_off),
               *Sin = reinterpret_cast<float *>(ws + L.sin_off);
@@ -1265,8 +1359,8 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
             e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, nullptr, nullptr, M, recs,
                                 stream, zero_page);
         if (e == hipSuccess) {
-            hipLaunchKernelGGL(k_scan_combine, dim3((unsigned)(64 * ((H + 7) / 8))), dim3(512), 0, stream, P, H,
-                               initial_state, R, M, Sin, final_state);
+            hipLaunchKernelGGL(k_scan_combine, dim3((unsigned)(64 * ((n_seq * H + 7) / 8))), dim3(512), 0, stream,
+                               (int)n_seq, H, seg0, initial_state, R, M, Sin, final_state);
             e = hipGetLastError();
         }
         if (e == hipSuccess)  // D (its final states land in R, no longer needed)

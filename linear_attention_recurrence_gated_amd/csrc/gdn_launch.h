@@ -31,6 +31,8 @@ hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k,
 // or the chunk-level scan (one sequence).
 enum { CHUNKED_AUTO = 0, CHUNKED_CHAIN = 1, CHUNKED_SCAN = 2 };
 size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H, int mode);
+// Whether CHUNKED_SCAN takes this batch: 1 to 64 sequences, at least one token.
+bool prefill_chunked_scan_supported(int64_t n_seq, int64_t total_tokens);
 hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v,
                                   const float *g, const float *beta, const int32_t *cu_seqlens,
                                   const int32_t *cu_seqlens_host, int64_t n_seq,

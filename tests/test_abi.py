@@ -271,14 +271,30 @@ def test_decode_slots_host_checks():
 
 
 def test_scan_mode_validation():
-    # the scan takes one sequence of at least 128 tokens
+    # the scan takes 1 to 64 sequences and at least one token
+    cu = np.arange(66, dtype=np.int32) * 10
+    st, msg = _prefill(chunk=gdn.CHUNK_64_SCAN, dtype=gdn.GDN_BF16, dk=128, dv=128, cu=FAKE * 512,
+                       cu_host=_host(cu), n_seq=65, N=650)
+    assert st == 7, msg
+    st, msg = _prefill(chunk=gdn.CHUNK_64_SCAN, dtype=gdn.GDN_BF16, dk=128, dv=128, N=0)
+    assert st == 7, msg
+    # two sequences pass that check and stop at the missing workspace (nothing is launched)
     cu = np.array([0, 100, 300], np.int32)
     st, msg = _prefill(chunk=gdn.CHUNK_64_SCAN, dtype=gdn.GDN_BF16, dk=128, dv=128, cu=FAKE * 512,
                        cu_host=_host(cu), n_seq=2, N=300)
-    assert st == 7, msg
-    st, msg = _prefill(chunk=gdn.CHUNK_64_SCAN, dtype=gdn.GDN_BF16, dk=128, dv=128, N=100)
-    assert st == 7, msg
+    assert st == 6, msg
     assert gdn.prefill_algorithm(gdn.GDN_BF16, 128, 128, gdn.CHUNK_64_SCAN) == gdn.CHUNK_64_SCAN
     assert gdn.prefill_algorithm(gdn.GDN_FP32, 128, 128, gdn.CHUNK_64_SCAN) == 0
-    assert gdn.prefill_workspace_bytes(4096, 1, 4, 128, 128, gdn.GDN_BF16, gdn.CHUNK_64_SCAN) > \
+    # room for the scan's states: asked for, or possibly chosen (few heads, no more
+    # sequences than the segment budget 256 / (4 H))
+    ws = lambda n_seq, H, chunk: gdn.prefill_workspace_bytes(4096, n_seq, H, 128, 128, gdn.GDN_BF16, chunk)
+    state = 128 * 128 * 4
+    assert ws(1, 4, gdn.CHUNK_64_SCAN) >= ws(1, 4, gdn.CHUNK_64_CHAIN) + 3 * 16 * 4 * state
+    assert ws(2, 6, gdn.CHUNK_64) >= ws(2, 6, gdn.CHUNK_64_CHAIN) + 3 * 10 * 6 * state
+    assert ws(11, 6, gdn.CHUNK_64) == ws(11, 6, gdn.CHUNK_64_CHAIN)   # more sequences than the budget of 10
+    assert ws(11, 6, gdn.CHUNK_64_SCAN) >= ws(11, 6, gdn.CHUNK_64_CHAIN) + 3 * 11 * 6 * state
+    assert ws(1, 17, gdn.CHUNK_64) == ws(1, 17, gdn.CHUNK_64_CHAIN)   # a budget below 4 segments
+    assert ws(1, 16, gdn.CHUNK_64) > ws(1, 16, gdn.CHUNK_64_CHAIN)
+    assert ws(65, 1, gdn.CHUNK_64) == ws(65, 1, gdn.CHUNK_64_CHAIN)
+    assert ws(1, 4, gdn.CHUNK_64_SCAN) > \
         gdn.prefill_workspace_bytes(4096, 1, 4, 128, 128, gdn.GDN_BF16, gdn.CHUNK_64_CHAIN)

@@ -1,4 +1,4 @@
-"""GPU parity of the chunk-level scan (GDN_CHUNK_64_SCAN: one sequence cut
+"""GPU parity of the chunk-level scan (GDN_CHUNK_64_SCAN: each sequence cut
 into segments whose affine state maps are formed in parallel and combined in
 order) against the CPU oracle, next to the one-chain form on the same inputs."""
 import numpy as np
@@ -76,3 +76,41 @@ def test_auto_choice(oracle_lib):
     o_auto, s_auto = run(inp, gdn.CHUNK_64)
     o_scan, s_scan = run(inp, gdn.CHUNK_64_SCAN)
     assert np.array_equal(o_auto, o_scan) and np.array_equal(s_auto, s_scan)
+
+
+@pytest.mark.parametrize("lengths, H", [
+    ([700, 1500], 3),
+    ([64, 3000, 0, 700, 1], 3),       # an empty sequence, a one-token one, one of a single chunk
+    ([2048, 2048, 2048, 2048], 2),
+    ([130] * 12, 8),                  # more sequences than the segment budget of 8: one segment each
+    ([0, 900, 0], 4),
+])
+def test_several_sequences(oracle_lib, lengths, H):
+    say("scan sequences", lengths, "H =", H)
+    inp = w.make_prefill(lengths, H=H, d=128, seed=320 + H + len(lengths), gate_shift=-1.0, init_std=0.3,
+                         packed=True)
+    check(inp, f"{len(lengths)} sequences H={H}")
+
+
+def test_many_short_sequences_in_place(oracle_lib):
+    """64 sequences (the most the scan takes), some empty, updated in place."""
+    rng = np.random.default_rng(330)
+    lengths = [int(x) for x in rng.integers(0, 400, 64)]
+    lengths[5] = lengths[40] = 0
+    say("scan 64 sequences in place,", sum(lengths), "tokens")
+    inp = w.make_prefill(lengths, H=1, d=128, seed=331, gate_shift=-1.5, init_std=0.2, packed=True)
+    check(inp, "64 sequences", in_place=True)
+
+
+def test_auto_choice_several_sequences(oracle_lib):
+    """Two sequences with six heads: GDN_CHUNK_64 takes the scan (the same plan
+    as when asked for); eleven sequences exceed the segment budget and take
+    the chain."""
+    inp = w.make_prefill([4096, 3000], H=6, d=128, seed=332, gate_shift=2.0, init_std=0.1, packed=True)
+    o_auto, s_auto = run(inp, gdn.CHUNK_64)
+    o_scan, s_scan = run(inp, gdn.CHUNK_64_SCAN)
+    assert np.array_equal(o_auto, o_scan) and np.array_equal(s_auto, s_scan)
+    inp = w.make_prefill([300] * 11, H=6, d=128, seed=333, gate_shift=2.0, init_std=0.1, packed=True)
+    o_auto, s_auto = run(inp, gdn.CHUNK_64)
+    o_chain, s_chain = run(inp, gdn.CHUNK_64_CHAIN)
+    assert np.array_equal(o_auto, o_chain) and np.array_equal(s_auto, s_chain)
