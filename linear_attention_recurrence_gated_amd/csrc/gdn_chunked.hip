@@ -272,21 +272,38 @@ __device__ __forceinline__ u32x4_t rowfrag(const char *tile, int row0, int kj, i
     return *reinterpret_cast<const u32x4_t *>(tile + t * 256 + ((u ^ (t & 15)) << 4));
 }
 
-// Row fragment in slot order (slot 8g+e <-> column 32kj + slot_k(g, e)).
-__device__ __forceinline__ u32x4_t rowfrag_slots(const char *tile, int row0, int kj, int g4, int r) {
-    const int t = row0 + r, sw = t & 15, h = (g4 & 1) * 8;
-    const int u0 = 4 * kj + (g4 >> 1), u1 = u0 + 2;
-    const u32x2_t a = *reinterpret_cast<const u32x2_t *>(tile + t * 256 + ((u0 ^ sw) << 4) + h);
-    const u32x2_t b = *reinterpret_cast<const u32x2_t *>(tile + t * 256 + ((u1 ^ sw) << 4) + h);
-    return u32x4_t{a[0], a[1], b[0], b[1]};
-}
+// Columns of the state in the chains' accumulators.  Tile jm of S^T (16
+// columns) holds, in lane (g, r), S[row r][st_col(jm, g) + e], e = 0..3: tiles
+// 2 kk and 2 kk + 1 interleave the 32 columns of step kk in groups of four, so
+// that the two tiles stacked along k form a B fragment in natural column
+// order (slot 8g + e <-> column 32 kk + 8 g + e).  The products K S0^T and
+// Q S0^T then take their A fragments by single 16-byte reads (rowfrag).
+__device__ __forceinline__ int st_col(int jm, int g4) { return 32 * (jm >> 1) + 8 * g4 + 4 * (jm & 1); }
 
 // Token-major fragment of the transpose: lane (g, r) gets X[32ks + slot_k(g, e)][16cm + r], e = 0..7,
-// where X is the row tile (tokens x columns).  Two transposing loads of four tokens each.
+// where X is the row tile (tokens x columns).  Two transposing loads of four tokens each (lane
+// (e, m) of a group of 16 loads columns 4m .. 4m + 3 of token 4g + e; lane r receives column r).
 __device__ __forceinline__ u32x4_t colfrag(const char *tile, int ks, int cm, int g4, int lane) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     const int L = lane & 15, e = L >> 2, m = L & 3;
     const int unit = 2 * cm + (m >> 1), half = (m & 1) * 8;
+    const int t0 = 32 * ks + 4 * g4 + e, t1 = t0 + 16;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(tile + t0 * 256 + ((unit ^ (t0 & 15)) << 4) + half));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(tile + t1 * 256 + ((unit ^ (t1 & 15)) << 4) + half));
+    const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
+    return u32x4_t{a2[0], a2[1], b2[0], b2[1]};
+}
+
+// The same for the state tile cm of S^T in the permuted column order: lane
+// (g, r) gets X[32ks + slot_k(g, e)][32 (cm >> 1) + 8 (r >> 2) + 4 (cm & 1) + (r & 3)]
+// (lane (e, m) loads columns 32 (cm >> 1) + 8m + 4 (cm & 1) .. + 3).  As the A
+// operand of the state update it makes output row 4g + e column st_col(cm, g) + e.
+__device__ __forceinline__ u32x4_t colfrag_st(const char *tile, int ks, int cm, int g4, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int L = lane & 15, e = L >> 2, m = L & 3;
+    const int unit = 4 * (cm >> 1) + m, half = (cm & 1) * 8;
     const int t0 = 32 * ks + 4 * g4 + e, t1 = t0 + 16;
     const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16 *)(tile + t0 * 256 + ((unit ^ (t0 & 15)) << 4) + half));
@@ -673,12 +690,12 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
 
     const int iw = tile * 16 * NW + 16 * wave;  // first row of S (d_v index) owned by this wave
     const int it = iw >> 4;
-    // S^T in accumulators: St[jm] lane (g4, r) holds S[iw + r][16 jm + 4 g4 + e]
+    // S^T in accumulators: St[jm] lane (g4, r) holds S[iw + r][st_col(jm, g4) + e]
     f32x4_t St[8];
     const int64_t sbase = ((int64_t)s * H + h) * DK * DK + (int64_t)(iw + r) * DK;
 #pragma unroll
     for (int jm = 0; jm < 8; ++jm)
-        St[jm] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + 16 * jm + 4 * g4) : zero4();
+        St[jm] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + st_col(jm, g4)) : zero4();
 
     lds_barrier();  // chunk 0 is in buf[0]
     for (int c = 0; c < nc; ++c) {
@@ -702,8 +719,8 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
             O[tb] = zero4();
 #pragma unroll
             for (int kj = 0; kj < 4; ++kj) {
-                X[tb] = mfma2b(rowfrag_slots(B.K, 16 * tb, kj, g4, r), bSh[kj], bSl[kj], X[tb]);
-                O[tb] = mfma2b(rowfrag_slots(B.Q, 16 * tb, kj, g4, r), bSh[kj], bSl[kj], O[tb]);
+                X[tb] = mfma2b(rowfrag(B.K, 16 * tb, kj, g4, r), bSh[kj], bSl[kj], X[tb]);
+                O[tb] = mfma2b(rowfrag(B.Q, 16 * tb, kj, g4, r), bSh[kj], bSl[kj], O[tb]);
             }
         }
         // Y = V - diag(e^{G_{t-1}}) X, in accumulator layout (tiles 2 ks and 2 ks + 1 from one V^T fragment)
@@ -768,14 +785,15 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
         for (int jm = 0; jm < 8; ++jm) {
             St[jm] *= eGn;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) St[jm] = mfma2b(colfrag(B.K, ks, jm, g4, lane), bUh[ks], bUl[ks], St[jm]);
+            for (int ks = 0; ks < 2; ++ks)
+                St[jm] = mfma2b(colfrag_st(B.K, ks, jm, g4, lane), bUh[ks], bUl[ks], St[jm]);
         }
         lds_barrier();  // chunk c + 1 is in the other buffer, and this one is free
     }
 
     float *dst = final_state + sbase;
 #pragma unroll
-    for (int jm = 0; jm < 8; ++jm) *reinterpret_cast<f32x4_t *>(dst + 16 * jm + 4 * g4) = St[jm];
+    for (int jm = 0; jm < 8; ++jm) *reinterpret_cast<f32x4_t *>(dst + st_col(jm, g4)) = St[jm];
 }
 
 // ---------------------------------------------------------------------------
@@ -971,16 +989,16 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
 
     const int sl = wave >> 1, hf = wave & 1;  // row slice, column half
     const int iw = tile * 32 + 16 * sl;       // first row of S owned by this wave
-    // S^T in accumulators, this wave's 64 columns: St[j] lane (g4, r) holds S[iw + r][16 (4 hf + j) + 4 g4 + e]
+    // S^T in accumulators, this wave's 64 columns: St[j] lane (g4, r) holds S[iw + r][64 hf + st_col(j, g4) + e]
     f32x4_t St[4];
     const int64_t sbase = ((int64_t)s * H + h) * DK * DK + (int64_t)(iw + r) * DK + 64 * hf;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if (vz) {  // the homogeneous pass starts from S = I
 #pragma unroll
-            for (int e = 0; e < 4; ++e) St[j][e] = (iw + r == 16 * (4 * hf + j) + 4 * g4 + e) ? 1.f : 0.f;
+            for (int e = 0; e < 4; ++e) St[j][e] = (iw + r == 64 * hf + st_col(j, g4) + e) ? 1.f : 0.f;
         } else {
-            St[j] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + 16 * j + 4 * g4)
+            St[j] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + st_col(j, g4))
                                   : zero4();
         }
     }
@@ -1028,8 +1046,8 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             O[tb] = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                X[tb] = mfma2b(rowfrag_slots(B.K, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], X[tb]);
-                if (outs) O[tb] = mfma2b(rowfrag_slots(B.Q, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], O[tb]);
+                X[tb] = mfma2b(rowfrag(B.K, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], X[tb]);
+                if (outs) O[tb] = mfma2b(rowfrag(B.Q, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], O[tb]);
             }
             sm.xch[wave][tb][lane] = X[tb];
             sm.xch[wave][4 + tb][lane] = O[tb];
@@ -1106,14 +1124,14 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             St[j] *= eGn;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                St[j] = mfma2b(colfrag(B.K, ks, 4 * hf + j, g4, lane), bUh[ks], bUl[ks], St[j]);
+                St[j] = mfma2b(colfrag_st(B.K, ks, 4 * hf + j, g4, lane), bUh[ks], bUl[ks], St[j]);
         }
         lds_barrier();  // A_{c+1}: chunk c + 1 is in the other buffer, and this one is free
     }
 
     float *dst = final_state + sbase;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4_t *>(dst + 16 * j + 4 * g4) = St[j];
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4_t *>(dst + st_col(j, g4)) = St[j];
 }
 
 hipError_t launch_chain_cs(const void *q, const void *k, const void *v, const int32_t *cu, const int32_t *chunk_base,
