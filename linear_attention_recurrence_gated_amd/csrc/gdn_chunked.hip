@@ -1292,16 +1292,22 @@ int chain_waves(int64_t units) {
     return 4;  // measured faster than 2 even when 2 would fill more CUs (fewer record copies per head)
 }
 
-// The column-split chain (four workgroups per pair) when the (sequence, head)
-// pairs leave most CUs idle with two workgroups per pair; GDN_CHAIN_SPLIT=0|1
-// overrides (a tuning knob, read once).
-bool use_column_split(int64_t units) {
+// The column-split chain (four workgroups per pair, a shorter step per chunk)
+// when it runs every pair in little more than the longest pair's time: the
+// workgroups of the long sequences (more than half the longest's chunks) all
+// start at once on the 256 CUs, and the 4 H sum_s chunks_s workgroup-chunks
+// of the batch take at most 1.1 times max_s chunks_s steps there.  Past that
+// it is throughput-bound, and the two-workgroup form, with half the workgroups
+// and copies per pair, is faster (measured on packed batches of 8 sequences
+// of 1,224 to 54,318 tokens: 24 heads favour the column split, 48 heads the
+// two-workgroup form).  GDN_CHAIN_SPLIT=0|1 overrides (a tuning knob, read once).
+bool use_column_split(int64_t sum_chunks, int64_t max_chunks, int64_t n_long, int H) {
     static const int forced = [] {
         const char *e = getenv("GDN_CHAIN_SPLIT");
         return e ? atoi(e) : -1;
     }();
     if (forced == 0 || forced == 1) return forced == 1;
-    return units * CS_TILES <= 256;
+    return CS_TILES * (int64_t)H * n_long <= 256 && 10 * CS_TILES * (int64_t)H * sum_chunks <= 11 * 256 * max_chunks;
 }
 
 }  // namespace
@@ -1331,14 +1337,21 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     int32_t *chunk_base = cu_seqlens ? reinterpret_cast<int32_t *>(ws + L.base_off) : nullptr;
     int32_t *seq_order = cu_seqlens ? reinterpret_cast<int32_t *>(ws + L.order_off) : nullptr;
     char *recs = ws + L.rec_off;
-    int64_t n_chunks = 0;
+    int64_t n_chunks = 0, max_chunks = 0, n_long = 1;  // n_long: sequences of more than half max_chunks
     if (cu_seqlens) {
-        for (int64_t s = 0; s < n_seq; ++s) n_chunks += (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + C - 1) / C;
+        n_long = 0;
+        for (int64_t s = 0; s < n_seq; ++s) {
+            const int64_t nc = (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + C - 1) / C;
+            n_chunks += nc;
+            max_chunks = std::max(max_chunks, nc);
+        }
+        for (int64_t s = 0; s < n_seq; ++s)
+            n_long += 2 * ((cu_seqlens_host[s + 1] - cu_seqlens_host[s] + C - 1) / C) > max_chunks;
         hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, stream, cu_seqlens, (int)n_seq, chunk_base, seq_order);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else {
-        n_chunks = (total_tokens + C - 1) / C;
+        n_chunks = max_chunks = (total_tokens + C - 1) / C;
     }
     ScanSegs segs;
     if (sp.P > 0) {
@@ -1383,7 +1396,7 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
         }
         if (e == hipSuccess)  // D (its final states land in R, no longer needed)
             e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, Sin, o, R, recs, stream);
-    } else if (use_column_split(n_seq * H))
+    } else if (use_column_split(n_chunks, max_chunks, n_long, H))
         e = launch_chain_cs(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
                             final_state, recs, stream);
     else if (chain_waves(n_seq * H) == 4)
