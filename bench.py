@@ -345,10 +345,16 @@ def cpu_baseline(w, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": runs * T / el, "unit": "tokens/s/layer", "cores": threads, "kind": "oracle",
             "sample": f"full prefill workload (B=1, H=48, T=4096, d=128) run {runs}x in double precision, "
                       f"{el:.1f} s wall on {threads} host threads",
-            "gflops": runs * T * H * 6 * D * D / el / 1e9}
+            "gflops": runs * T * H * 6 * D * D / el / 1e9, "cpu_model": cpu_model}
 
 
 def pre_entry(pre_ms):
