@@ -38,7 +38,9 @@
 //                  rows are independent, so the waves and workgroups of one
 //                  head never exchange data.
 //   k_chunk_chain_cs  the same with four workgroups per (sequence, head) and
-//                  the columns of S split over pairs of waves, for few pairs.
+//                  the columns of S split over pairs of waves, when the batch's
+//                  pairs run in little more than the longest chain's time
+//                  (see use_column_split).
 //   k_scan_combine the chunk-level scan for few (sequence, head) pairs
 //                  (three k_chunk_chain_cs passes over segments, then a short
 //                  ordered combine of their affine maps); see below.

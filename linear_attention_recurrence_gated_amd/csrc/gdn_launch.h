@@ -28,7 +28,7 @@ hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k,
 
 // Chunkwise-parallel prefill (64-token chunks, d = 128, bf16 q/k/v).
 // Chunked prefill modes: the library's choice, one chain per (sequence, head),
-// or the chunk-level scan (one sequence).
+// or the chunk-level scan (up to 64 sequences cut into segments).
 enum { CHUNKED_AUTO = 0, CHUNKED_CHAIN = 1, CHUNKED_SCAN = 2 };
 size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H, int mode);
 // Whether CHUNKED_SCAN takes this batch: 1 to 64 sequences, at least one token.

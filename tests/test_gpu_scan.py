@@ -65,8 +65,8 @@ def test_variants(oracle_lib, variant):
 
 
 def test_auto_choice(oracle_lib):
-    """GDN_CHUNK_64 takes the scan for one sequence with few heads and the
-    chain otherwise; the scan asks for more workspace."""
+    """GDN_CHUNK_64 takes the scan for one sequence with few heads (and the
+    chain with many); the scan asks for more workspace."""
     small = gdn.prefill_workspace_bytes(4096, 1, 6, 128, 128, gdn.GDN_BF16, gdn.CHUNK_64)
     chain = gdn.prefill_workspace_bytes(4096, 1, 6, 128, 128, gdn.GDN_BF16, gdn.CHUNK_64_CHAIN)
     big = gdn.prefill_workspace_bytes(4096, 1, 48, 128, 128, gdn.GDN_BF16, gdn.CHUNK_64)
@@ -114,3 +114,14 @@ def test_auto_choice_several_sequences(oracle_lib):
     o_auto, s_auto = run(inp, gdn.CHUNK_64)
     o_chain, s_chain = run(inp, gdn.CHUNK_64_CHAIN)
     assert np.array_equal(o_auto, o_chain) and np.array_equal(s_auto, s_chain)
+
+
+@pytest.mark.parametrize("variant", [gdn.GDN_VARIANT_NO_GATE, gdn.GDN_VARIANT_NO_ERASE,
+                                     gdn.GDN_VARIANT_NO_GATE | gdn.GDN_VARIANT_NO_ERASE])
+def test_several_sequences_variants(oracle_lib, variant):
+    say("scan sequences, variant", variant)
+    inp = w.make_prefill([900, 0, 1300, 64], H=3, d=128, seed=340 + variant, gate_shift=-1.0, init_std=0.2,
+                         packed=True)
+    if variant & gdn.GDN_VARIANT_NO_ERASE:
+        inp.beta[:] = inp.beta * np.float32(0.05)
+    check(inp, f"sequences variant {variant}", variant=variant, in_place=True)
