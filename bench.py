@@ -12,8 +12,12 @@ initial state (initial_state NULL: the kernels start from zeros), writing o
 and the final state.  The decode half is timed as one pass of 256
 gdn_decode_step calls.  Further entries time the pre-processing, the serving
 form of the decode step and the chunk-level scan.  Timing uses HIP events recorded on the stream every kernel is launched
-on (torch's current stream).  The CPU oracle (test infrastructure) is timed on
-the host's cores as a reported baseline.
+on (torch's current stream): the reported means time each series of calls as
+one block (one event pair around back-to-back calls); percentiles come from a
+second series with an event pair around each call; the prefill's per-kernel
+times come from events the library records between its two kernels.  The CPU
+oracle (test infrastructure) is timed on the host's cores as a reported
+baseline.
 
 Prints one JSON line.
 """
@@ -97,6 +101,35 @@ def run_conditions(torch):
     return cond
 
 
+def time_block(torch, fn, steps):
+    """Mean ms per call of `steps` back-to-back calls fn(0) .. fn(steps - 1) on
+    the current stream, bracketed by one pair of events with a synchronize on
+    both sides (no event between the calls: an event record leaves the GPU
+    idle for several microseconds).  Returns (ms per call, wall seconds)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record()
+    for i in range(steps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps, time.perf_counter() - t0
+
+
+def time_each(torch, fn, steps):
+    """Sorted ms of `steps` calls fn(i), each bracketed by its own pair of
+    events (for percentiles; includes the events' own idle time)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
+
+
 def bench_prefill(torch, gdn, w, steps, warmup, rotate):
     """Times `steps` prefill steps cycling over `rotate` resident copies of the
     inputs and outputs (rotate > 1 keeps the 256 MB last-level cache from
@@ -126,17 +159,8 @@ def bench_prefill(torch, gdn, w, steps, warmup, rotate):
 
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    for i, (a, b) in enumerate(ev):
-        a.record()
-        step(i)
-        b.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    block_ms, wall = time_block(torch, step, steps)
+    ms = time_each(torch, step, steps)
     # the prefill call alone, with events between its kernels (library marks):
     # [0] before the first kernel, [1] after the per-chunk preparation, [2] after the chain
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -151,7 +175,7 @@ def bench_prefill(torch, gdn, w, steps, warmup, rotate):
     ms_call = {"call": sorted(m[0].elapsed_time(m[2]) for m in marks),
                "k_chunk_prep": sorted(m[0].elapsed_time(m[1]) for m in marks),
                "k_chunk_chain": sorted(m[1].elapsed_time(m[2]) for m in marks)}
-    return ms, ms_call, wall
+    return block_ms, ms, ms_call, wall
 
 
 def bench_decode(torch, gdn, w, steps, rotate):
@@ -169,30 +193,28 @@ def bench_decode(torch, gdn, w, steps, rotate):
     states = [torch.empty_like(s0) for _ in range(rotate)]
     o = torch.empty((steps, DEC_B, H, D), dtype=torch.float32, device=dev)
 
-    def one_pass(events=None):
+    def init():
         for st in states:
             gdn.state_init(st, s0)
-        for t in range(steps):
-            if events is not None:
-                events[t][0].record()
-            gdn.decode_step(q[t], k[t], v[t], g[t], beta[t], states[t % rotate], out=o[t])
-            if events is not None:
-                events[t][1].record()
 
-    one_pass()  # warm-up pass
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    one_pass(ev)
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in ev)
-    return ms
+    def step(t):
+        gdn.decode_step(q[t], k[t], v[t], g[t], beta[t], states[t % rotate], out=o[t])
+
+    init()
+    for t in range(steps):  # warm-up pass
+        step(t)
+    init()
+    block_ms, _ = time_block(torch, step, steps)
+    init()
+    ms = time_each(torch, step, steps)
+    return block_ms, ms
 
 
 def bench_scan(torch, gdn, w, steps, warmup):
     """One sequence with few heads: the per-GPU share of the one-layer prefill
     when its 48 heads are split over 8 GPUs (H = 6, T = 4096), and the same at
     T = 16384; each timed with the one-chain form and with the chunk-level
-    scan (event-bracketed calls, inputs resident).  Returns a dict."""
+    scan (back-to-back calls timed as a block, inputs resident).  Returns a dict."""
     import numpy as np
     dev = "cuda:0"
     out = {}
@@ -210,14 +232,7 @@ def bench_scan(torch, gdn, w, steps, warmup):
             call = lambda: gdn.prefill(q, k, v, g, beta, chunk=ch, out=o, final_state=st, workspace=ws)
             for _ in range(warmup):
                 call()
-            torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-            for a, b in ev:
-                a.record()
-                call()
-                b.record()
-            torch.cuda.synchronize()
-            row[name + "_ms"] = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            row[name + "_ms"], _ = time_block(torch, lambda i: call(), steps)
         row["speedup"] = row["chain_ms"] / row["scan_ms"]
         row["scan_tokens_per_s"] = T_ / (row["scan_ms"] / 1e3)
         out[f"H6_T{T_}"] = row
@@ -248,14 +263,8 @@ def bench_decode_slots(torch, gdn, w, steps, rotate):
     def timed(fns):
         for f in fns:
             f()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for t, (a, b) in enumerate(ev):
-            a.record()
-            fns[t % len(fns)]()
-            b.record()
-        torch.cuda.synchronize()
-        return sorted(a.elapsed_time(b) for a, b in ev)
+        fn = lambda t: fns[t % len(fns)]()
+        return time_block(torch, fn, steps)[0], time_each(torch, fn, steps)
 
     eager = timed([lambda p=p: step(p) for p in pools])
     graphs = []
@@ -290,14 +299,7 @@ def bench_preprocess(torch, gdn, w, steps, warmup, rotate):
 
     for i in range(warmup):
         call(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i, (a, b) in enumerate(ev):
-        a.record()
-        call(i)
-        b.record()
-    torch.cuda.synchronize()
-    return sorted(a.elapsed_time(b) for a, b in ev)
+    return time_block(torch, call, steps)[0], time_each(torch, call, steps)
 
 
 def bench_copy(torch, gdn, mib, reps):
@@ -357,10 +359,10 @@ def cpu_baseline(w, seconds):
             "gflops": runs * T * H * 6 * D * D / el / 1e9, "cpu_model": cpu_model}
 
 
-def pre_entry(pre_ms):
+def pre_entry(pre_block_ms, pre_ms):
     """Pre-processing (convolution, SiLU, norm, gate maps) at T = 4096, H = 48."""
     nbytes = PRE_BYTES_PER_TOKEN_HEAD * T * H + PRE_BYTES_FIXED
-    ms = mean(pre_ms)
+    ms = pre_block_ms
     gbs = nbytes / (ms / 1e3) / 1e9
     return {"mean_ms": ms, "p50_ms": pct(pre_ms, 50), "tokens_per_s_layer": T / (ms / 1e3),
             "roofline": {"kernel": "k_preprocess (one gdn_preprocess call; it returns the conv state itself)",
@@ -408,31 +410,34 @@ def main():
             ap.error(f"--only: unknown part(s) {bad}")
         for part in parts:
             if part == "prefill":
-                ms, ms_call, _ = bench_prefill(torch, gdn, w, args.steps, args.warmup, args.rotate)
-                print(json.dumps({"only": "prefill", "ms_per_step": mean(ms),
+                block_ms, ms, ms_call, _ = bench_prefill(torch, gdn, w, args.steps, args.warmup, args.rotate)
+                print(json.dumps({"only": "prefill", "ms_per_step": block_ms, "event_bracketed_mean_ms": mean(ms),
                                   **{k + "_mean_ms": mean(x) for k, x in ms_call.items()}}), flush=True)
             elif part == "decode":
-                dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
-                print(json.dumps({"only": "decode", "ms_per_step": mean(dec_ms)}), flush=True)
+                dec_block_ms, dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
+                print(json.dumps({"only": "decode", "ms_per_step": dec_block_ms,
+                                  "event_bracketed_mean_ms": mean(dec_ms)}), flush=True)
             elif part == "decode_slots":
-                ds_ms, dg_ms = bench_decode_slots(torch, gdn, w, args.decode_steps, args.rotate)
-                print(json.dumps({"only": "decode_slots", "ms_per_step": mean(ds_ms),
-                                  "graph_replay_ms_per_step": mean(dg_ms)}), flush=True)
+                (ds_block, ds_ms), (dg_block, dg_ms) = bench_decode_slots(torch, gdn, w, args.decode_steps,
+                                                                          args.rotate)
+                print(json.dumps({"only": "decode_slots", "ms_per_step": ds_block,
+                                  "graph_replay_ms_per_step": dg_block}), flush=True)
             elif part == "scan":
                 print(json.dumps({"only": "scan", **bench_scan(torch, gdn, w, args.steps, args.warmup)}), flush=True)
             elif part == "preprocess":
-                pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
-                print(json.dumps({"only": "preprocess", "ms_per_call": mean(pre_ms)}), flush=True)
+                pre_block, pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
+                print(json.dumps({"only": "preprocess", "ms_per_call": pre_block,
+                                  "event_bracketed_mean_ms": mean(pre_ms)}), flush=True)
             else:
                 print(json.dumps(bench_copy(torch, gdn, args.copy_mib, max(1, args.steps))), flush=True)
         return
-    ms, ms_call, wall = bench_prefill(torch, gdn, w, args.steps, args.warmup, args.rotate)
-    dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
-    pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
-    ds_ms, dg_ms = bench_decode_slots(torch, gdn, w, args.decode_steps, args.rotate)
+    block_ms, ms, ms_call, wall = bench_prefill(torch, gdn, w, args.steps, args.warmup, args.rotate)
+    dec_block_ms, dec_ms = bench_decode(torch, gdn, w, args.decode_steps, args.rotate)
+    pre_block, pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
+    (ds_block, ds_ms), (dg_block, dg_ms) = bench_decode_slots(torch, gdn, w, args.decode_steps, args.rotate)
     scan = bench_scan(torch, gdn, w, min(args.steps, 20), args.warmup)
 
-    step_ms = mean(ms)
+    step_ms = block_ms
     tok_s = T / (step_ms / 1e3)
     prep_ms, chain_ms, call_ms = mean(ms_call["k_chunk_prep"]), mean(ms_call["k_chunk_chain"]), mean(ms_call["call"])
     prefill_bytes = PREFILL_BYTES_PER_TOKEN_HEAD * T * H + 2 * STATE_BYTES_PER_HEAD * H
@@ -447,7 +452,7 @@ def main():
     if tp is not None and tc is not None:
         traffic = tp + tc
 
-    dec_step_ms = mean(dec_ms)
+    dec_step_ms = dec_block_ms
     dec_bytes = DECODE_BYTES_PER_HEAD_TOKEN * DEC_B * H
     dec_gbs = dec_bytes / (dec_step_ms / 1e3) / 1e9
 
@@ -469,7 +474,8 @@ def main():
                                "sequences x 48 heads; successive steps cycle over `rotate` resident copies",
                    "batch": 1, "seq_len": T, "heads": H, "head_dim": D, "chunk": C,
                    "decode_batch": DEC_B, "decode_steps": args.decode_steps, "state_dtype": "fp32"},
-        "prefill": {"p50_ms": pct(ms, 50), "p95_ms": pct(ms, 95), "p99_ms": pct(ms, 99), "mean_ms": step_ms,
+        "prefill": {"mean_ms": step_ms, "p50_ms": pct(ms, 50), "p95_ms": pct(ms, 95), "p99_ms": pct(ms, 99),
+                    "event_bracketed_mean_ms": mean(ms),
                     "call_mean_ms": call_ms, "algorithmic_tflops": ach_tflops,
                     "mfma_frac": ach_tflops / BF16_MFMA_PEAK_TFLOPS,
                     "mfma_frac_full_tiles": PREFILL_FLOP_FULL_PER_TOKEN_HEAD * T * H / (call_ms / 1e3) / 1e12
@@ -488,33 +494,34 @@ def main():
                      "achieved": ach_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": prefill_bytes, "mean_ms": kern_ms},
         "decode": {"value": dec_gbs, "unit": "GB/s", "pct_hbm_peak": 100.0 * dec_gbs / HBM_PEAK_GBS,
-                   "ms_per_step": dec_step_ms, "p50_ms": pct(dec_ms, 50), "p95_ms": pct(dec_ms, 95),
+                   "ms_per_step": dec_step_ms, "event_bracketed_mean_ms": mean(dec_ms),
+                   "p50_ms": pct(dec_ms, 50), "p95_ms": pct(dec_ms, 95),
                    "p99_ms": pct(dec_ms, 99), "tokens_per_s_layer": DEC_B / (dec_step_ms / 1e3),
                    "roofline": {"kernel": "k_decode_step", "bound": "hbm", "achieved": dec_gbs,
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                                 "traffic": load_traffic("k_decode_step")}},
-        "preprocess": pre_entry(pre_ms),
+        "preprocess": pre_entry(pre_block, pre_ms),
         "scan": {"workload": "one sequence, H = 6 (48 heads over 8 GPUs), d = 128, bf16: one-chain form vs the "
                              "chunk-level scan", **scan},
-        "decode_slots": {"ms_per_step": mean(ds_ms), "p50_ms": pct(ds_ms, 50), "p99_ms": pct(ds_ms, 99),
-                         "value": dec_bytes / (mean(ds_ms) / 1e3) / 1e9, "unit": "GB/s",
-                         "frac_hbm_peak": dec_bytes / (mean(ds_ms) / 1e3) / 1e9 / HBM_PEAK_GBS,
-                         "graph_replay_ms_per_step": mean(dg_ms),
+        "decode_slots": {"ms_per_step": ds_block, "p50_ms": pct(ds_ms, 50), "p99_ms": pct(ds_ms, 99),
+                         "value": dec_bytes / (ds_block / 1e3) / 1e9, "unit": "GB/s",
+                         "frac_hbm_peak": dec_bytes / (ds_block / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "graph_replay_ms_per_step": dg_block, "graph_replay_p50_ms": pct(dg_ms, 50),
                          "workload": "config-3 step, 64 rows on a permutation of 64 of 128 pool slots; eager "
-                                     "launches, and replays of a captured HIP graph (event-bracketed)"},
+                                     "launches, and replays of a captured HIP graph (each timed as a block of back-to-back steps)"},
         "rotate": args.rotate,
         "conditions": run_conditions(torch),
     }
     if args.warm:
         # the same with one resident copy (inputs and state may be served from the last-level cache)
-        ms_warm, ms_call_warm, _ = bench_prefill(torch, gdn, w, args.steps, args.warmup, 1)
-        dec_ms_warm = bench_decode(torch, gdn, w, args.decode_steps, 1)
+        block_warm, _, ms_call_warm, _ = bench_prefill(torch, gdn, w, args.steps, args.warmup, 1)
+        dec_block_warm, _ = bench_decode(torch, gdn, w, args.decode_steps, 1)
         out["warm_single_copy"] = {
-            "prefill_ms_per_step": mean(ms_warm), "prefill_tokens_per_s_layer": T / (mean(ms_warm) / 1e3),
+            "prefill_ms_per_step": block_warm, "prefill_tokens_per_s_layer": T / (block_warm / 1e3),
             "k_chunk_prep_ms": mean(ms_call_warm["k_chunk_prep"]),
             "k_chunk_chain_ms": mean(ms_call_warm["k_chunk_chain"]),
-            "decode_ms_per_step": mean(dec_ms_warm),
-            "decode_gbs": dec_bytes / (mean(dec_ms_warm) / 1e3) / 1e9}
+            "decode_ms_per_step": dec_block_warm,
+            "decode_gbs": dec_bytes / (dec_block_warm / 1e3) / 1e9}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
