@@ -119,10 +119,10 @@ bool scan_possible(int mode, int64_t n_seq, int H) {
 
 // Plan the segments from the host copy of the offsets (NULL: one sequence).
 // The segment length cps is the one that minimises the estimated time, in
-// units of one chunk of the column-split chain (about 2.1 us, measured): the
-// three passes over cps chunks (2.75 together), a combine step (0.85) per
-// segment of the most-cut sequence, and 8.5 of fixed cost, against the chain's
-// max_s chunks_s.  Returns false when there is nothing to cut, more non-empty
+// units of one chunk of the column-split chain (about 2.0 us, measured): the
+// paired pass and the output pass over cps chunks (1.1 each), a combine step
+// (0.9) per segment of the most-cut sequence, and 5.5 of fixed cost (the
+// passes' start and tail), against the chain's max_s chunks_s.  Returns false when there is nothing to cut, more non-empty
 // sequences than segments fit, or (unless forced) no expected gain of 15%.
 // Segments fit: the budget (the passes fill the CUs once), or when forced
 // the workspace's capacity.
@@ -140,9 +140,9 @@ bool plan_scan(const int32_t *cu_host, int64_t n_seq, int64_t N, int H, bool for
     double best = 1e30;
     int64_t best_cps = 0;
     // the longest sequence alone needs cps >= nc_max / target; past the first
-    // feasible cps the cost grows by at least 2.75 - 0.85 per step
+    // feasible cps the cost grows by at least 2.2 - 0.9 per step
     for (int64_t cps = std::max<int64_t>(1, (nc_max + target - 1) / target); cps <= nc_max; ++cps) {
-        if (2.75 * (double)cps + 0.85 + 8.5 >= best) break;
+        if (2.2 * (double)cps + 0.9 + 5.5 >= best) break;
         int64_t P = 0, pmax = 0;
         for (int64_t s = 0; s < n_seq; ++s) {
             const int64_t ps = (chunks(s) + cps - 1) / cps;
@@ -150,7 +150,7 @@ bool plan_scan(const int32_t *cu_host, int64_t n_seq, int64_t N, int H, bool for
             pmax = std::max(pmax, ps);
         }
         if (P > target) continue;
-        const double cost = 2.75 * (double)cps + 0.85 * (double)pmax + 8.5;
+        const double cost = 2.2 * (double)cps + 0.9 * (double)pmax + 5.5;
         if (cost < best) {
             best = cost;
             best_cps = cps;
@@ -181,7 +181,7 @@ bool plan_scan(const int32_t *cu_host, int64_t n_seq, int64_t N, int H, bool for
 struct WsLayout {
     size_t base_off, order_off, rec_off, total;
     int scan_cap = 0;  // segments the scan's area holds (0: no scan area)
-    size_t seg_cu_off, seg_base_off, seg0_off, zero_off, r_off, m_off, sin_off;
+    size_t seg_cu_off, seg_base_off, seg0_off, r_off, m_off, sin_off;
 };
 
 WsLayout ws_layout(int64_t total_tokens, int64_t n_seq, int H, bool scan_area) {
@@ -198,8 +198,7 @@ WsLayout ws_layout(int64_t total_tokens, int64_t n_seq, int H, bool scan_area) {
         L.seg_cu_off = L.total;
         L.seg_base_off = L.seg_cu_off + up((SCAN_MAX_SEGMENTS + 1) * 4);
         L.seg0_off = L.seg_base_off + up((SCAN_MAX_SEGMENTS + 1) * 4);
-        L.zero_off = L.seg0_off + up((SCAN_MAX_SEGMENTS + 1) * 4);
-        L.r_off = L.zero_off + 256;
+        L.r_off = L.seg0_off + up((SCAN_MAX_SEGMENTS + 1) * 4);
         L.m_off = L.r_off + states;
         L.sin_off = L.m_off + states;
         L.total = L.sin_off + states;
@@ -377,11 +376,10 @@ __device__ __forceinline__ float4 t4(const char *qt, int t, int s4) {  // T[t][s
 }
 
 // Segments of the chunk-level scan (cu == NULL: no scan): the plan's token
-// and chunk offsets and first segment per sequence, and a zero page; written
-// to the workspace by the first workgroup of k_chunk_prep.
+// and chunk offsets and first segment per sequence, written to the workspace
+// by the first workgroup of k_chunk_prep.
 struct ScanSegs {
     int32_t *cu = nullptr, *base = nullptr, *seg0 = nullptr;
-    uint32_t *zero_page = nullptr;
     int P = 0, n_seq = 0;
     int32_t h_cu[SCAN_MAX_SEGMENTS + 1], h_base[SCAN_MAX_SEGMENTS + 1], h_seg0[SCAN_MAX_SEGMENTS + 1];
 };
@@ -398,7 +396,6 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
             segs.base[i] = segs.h_base[i];
         }
         for (int i = threadIdx.x; i <= segs.n_seq; i += 256) segs.seg0[i] = segs.h_seg0[i];
-        if (threadIdx.x < 64) segs.zero_page[threadIdx.x] = 0u;
     }
     const int64_t gc = blockIdx.x / H;
     const int h = blockIdx.x % H;
@@ -902,16 +899,18 @@ __device__ __forceinline__ const uint32_t *chunk_line(const char *rec, const uin
     return reinterpret_cast<const uint32_t *>(base + rowbase + (uint32_t)(min(row, n - 1) * rs + half * 64));
 }
 
-// vz: NULL, or a page of at least 64 zero bytes that stands in for every row
-// of v; the chain then runs the homogeneous part of the update (v = 0) from
-// S = I, and initial_state is not read.  OUTS = false: only the final states
-// are formed (no read-out products, no stores of o; o is not used).
-template <bool OUTS>
+// Modes: CS_OUT forms o and the final states.  CS_PAIR forms no read-out (no
+// products for it, no stores of o; o is not used) and carries two states
+// through the same chunks: one from initial_state (zeros if NULL) with the
+// real v into final_state, and one from S = I with v = 0 (the homogeneous
+// part of the update, the product of the chunks' transitions) into final_m.
+enum { CS_OUT = 0, CS_PAIR = 1 };
+template <int MODE>
 __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ seq_order,
     int n_seq, int64_t total_tokens, int H, const float *initial_state, float *__restrict__ o, float *final_state,
-    const char *__restrict__ recs, const uint16_t *__restrict__ vz) {
+    const char *__restrict__ recs, float *__restrict__ final_m) {
     const int bid = blockIdx.x;
     // All workgroups of one (sequence, head) share bid % 8, so they run on one XCD and share its L2.
     const int u = (bid / (8 * CS_TILES)) * 8 + (bid & 7);
@@ -927,7 +926,8 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
     const int rs = H * DK;
     const int vcol0 = tile * 32;  // the workgroup's first row of S = first column of v
-    constexpr bool outs = OUTS;  // false: the state only (no read-out)
+    constexpr bool outs = MODE == CS_OUT;  // false: no read-out
+    constexpr bool pair = MODE == CS_PAIR;  // a second state from S = I with v = 0
 
     __shared__ __attribute__((aligned(16))) ChainSmemCS sm;
 
@@ -938,7 +938,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             const int n = (int)min((int64_t)C, L - (int64_t)c * C);
             const int64_t rowbase = (t0 * H + h) * DK;
             cs_copies(sm.buf[c & 1], sm.scratch, recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q + rowbase,
-                      k + rowbase, vz ? vz : v + rowbase + vcol0, rs, vz ? 0 : rs, n, lane, cw, half);
+                      k + rowbase, v + rowbase + vcol0, rs, rs, n, lane, cw, half);
         };
         // Touch chunk c: the first 16 bytes of each 128-byte line in this
         // workgroup's quarter of the lines (the four workgroups of a pair share
@@ -947,7 +947,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         // re-touch line 0, so every wave issues exactly one load.
         auto touch = [=](int c) {
             int line = tile + CS_TILES * (cw * 64 + lane);
-            if (line >= PF_LINES || (vz && line >= REC_BYTES / 128 + 4 * C)) line = 0;  // no v lines to touch
+            if (line >= PF_LINES) line = 0;
             const int64_t t0 = seq_t0 + (int64_t)c * C;
             const int n = (int)min((int64_t)C, L - (int64_t)c * C);
             const uint32_t *src = chunk_line(recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q, k, v,
@@ -992,17 +992,15 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     const int sl = wave >> 1, hf = wave & 1;  // row slice, column half
     const int iw = tile * 32 + 16 * sl;       // first row of S owned by this wave
     // S^T in accumulators, this wave's 64 columns: St[j] lane (g4, r) holds S[iw + r][64 hf + st_col(j, g4) + e]
-    f32x4_t St[4];
+    f32x4_t St[4], Sm[4];  // Sm: the pair's second state (CS_PAIR only)
     const int64_t sbase = ((int64_t)s * H + h) * DK * DK + (int64_t)(iw + r) * DK + 64 * hf;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        if (vz) {  // the homogeneous pass starts from S = I
+        f32x4_t eye;  // S = I
 #pragma unroll
-            for (int e = 0; e < 4; ++e) St[j][e] = (iw + r == 64 * hf + st_col(j, g4) + e) ? 1.f : 0.f;
-        } else {
-            St[j] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + st_col(j, g4))
-                                  : zero4();
-        }
+        for (int e = 0; e < 4; ++e) eye[e] = (iw + r == 64 * hf + st_col(j, g4) + e) ? 1.f : 0.f;
+        St[j] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + st_col(j, g4)) : zero4();
+        Sm[j] = pair ? eye : zero4();
     }
     // output tiles of this wave: {0, 3} or {1, 2} (balanced P U work)
     const int ta = hf ? 1 : 0, tz = hf ? 2 : 3;
@@ -1038,9 +1036,13 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         }
 
         // partial X = K S0^T and Q S0^T over this wave's 64 columns (k steps 2 hf, 2 hf + 1)
-        u32x4_t bSh[2], bSl[2];
+        u32x4_t bSh[2], bSl[2], bMh[2], bMl[2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) split_pair(St[2 * kk], St[2 * kk + 1], bSh[kk], bSl[kk]);
+        for (int kk = 0; kk < 2; ++kk) {
+            split_pair(St[2 * kk], St[2 * kk + 1], bSh[kk], bSl[kk]);
+            if (pair) split_pair(Sm[2 * kk], Sm[2 * kk + 1], bMh[kk], bMl[kk]);
+        }
+        // O: Q S0^T (CS_OUT), or the pair's K Sm^T (CS_PAIR), exchanged in the same slots
         f32x4_t X[4], O[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -1048,8 +1050,10 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             O[tb] = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                X[tb] = mfma2b(rowfrag(B.K, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], X[tb]);
+                const u32x4_t kf = rowfrag(B.K, 16 * tb, 2 * hf + kk, g4, r);
+                X[tb] = mfma2b(kf, bSh[kk], bSl[kk], X[tb]);
                 if (outs) O[tb] = mfma2b(rowfrag(B.Q, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], O[tb]);
+                if (pair) O[tb] = mfma2b(kf, bMh[kk], bMl[kk], O[tb]);
             }
             sm.xch[wave][tb][lane] = X[tb];
             sm.xch[wave][4 + tb][lane] = O[tb];
@@ -1058,7 +1062,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             X[tb] += sm.xch[wave ^ 1][tb][lane];
-            if (tb == ta || tb == tz) O[tb] += sm.xch[wave ^ 1][4 + tb][lane];  // static indices, uniform test
+            if (pair || tb == ta || tb == tz) O[tb] += sm.xch[wave ^ 1][4 + tb][lane];  // static indices, uniform test
         }
 
         // Y = V - diag(e^{G_{t-1}}) X
@@ -1078,14 +1082,31 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             }
             split_pair(y[0], y[1], bYh[ks], bYl[ks]);
         }
-        // U = T Y
-        f32x4_t U[4];
+        // U = T Y (and the pair's Um = T Ym, Ym = -diag(e^{G_{t-1}}) Xm)
+        u32x4_t bYmh[2], bYml[2];
+        if (pair) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                f32x4_t y[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int tb = 2 * ks + hh;
+                    const f32x4_t em = *reinterpret_cast<const f32x4_t *>(gate + GATE_EGM1 + 16 * tb + 4 * g4);
+                    y[hh] = -(em * O[tb]);
+                }
+                split_pair(y[0], y[1], bYmh[ks], bYml[ks]);
+            }
+        }
+        f32x4_t U[4], Um[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             U[tb] = zero4();
+            Um[tb] = zero4();
 #pragma unroll
-            for (int ks = 0; ks <= (tb >> 1); ++ks)
+            for (int ks = 0; ks <= (tb >> 1); ++ks) {
                 U[tb] = mfma3(tfh[tblk(tb, ks)], tfl[tblk(tb, ks)], bYh[ks], bYl[ks], U[tb]);
+                if (pair) Um[tb] = mfma3(tfh[tblk(tb, ks)], tfl[tblk(tb, ks)], bYmh[ks], bYml[ks], Um[tb]);
+            }
         }
         // O = diag(e^{G_t}) Q S0^T + P U for this wave's two tiles
         u32x4_t bUh[2], bUl[2];
@@ -1116,17 +1137,29 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         }
 
         // S0^T <- e^{G_n} S0^T + K^T diag(beta_t e^{G_n - G_t}) U, this wave's 64 columns
+        u32x4_t bUmh[2], bUml[2];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) U[tb] *= *reinterpret_cast<const f32x4_t *>(gate + GATE_BW + 16 * tb + 4 * g4);
+        for (int tb = 0; tb < 4; ++tb) {
+            const f32x4_t bw = *reinterpret_cast<const f32x4_t *>(gate + GATE_BW + 16 * tb + 4 * g4);
+            U[tb] *= bw;
+            if (pair) Um[tb] *= bw;
+        }
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
+        for (int ks = 0; ks < 2; ++ks) {
+            split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
+            if (pair) split_pair(Um[2 * ks], Um[2 * ks + 1], bUmh[ks], bUml[ks]);
+        }
         const float eGn = gate[GATE_EGN];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             St[j] *= eGn;
+            if (pair) Sm[j] *= eGn;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                St[j] = mfma2b(colfrag_st(B.K, ks, 4 * hf + j, g4, lane), bUh[ks], bUl[ks], St[j]);
+            for (int ks = 0; ks < 2; ++ks) {
+                const u32x4_t kf = colfrag_st(B.K, ks, 4 * hf + j, g4, lane);
+                St[j] = mfma2b(kf, bUh[ks], bUl[ks], St[j]);
+                if (pair) Sm[j] = mfma2b(kf, bUmh[ks], bUml[ks], Sm[j]);
+            }
         }
         lds_barrier();  // A_{c+1}: chunk c + 1 is in the other buffer, and this one is free
     }
@@ -1134,19 +1167,27 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     float *dst = final_state + sbase;
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4_t *>(dst + st_col(j, g4)) = St[j];
+    if (pair) {
+        float *dm = final_m + sbase;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4_t *>(dm + st_col(j, g4)) = Sm[j];
+    }
 }
 
+// o != NULL: the outputs and final states (CS_OUT); o == NULL: the pair of
+// states into final_state and final_m (CS_PAIR).
 hipError_t launch_chain_cs(const void *q, const void *k, const void *v, const int32_t *cu, const int32_t *chunk_base,
                            const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H,
                            const float *initial_state, float *o, float *final_state, const char *recs,
-                           hipStream_t stream, const uint16_t *vz = nullptr) {
+                           hipStream_t stream, float *final_m = nullptr) {
     const int64_t units = n_seq * H;
     const int64_t grid = ((units + 7) / 8) * 8 * CS_TILES;
-    auto kern = o ? k_chunk_chain_cs<true> : k_chunk_chain_cs<false>;  // o == NULL: final states only
+    if (!o && !final_m) return hipErrorInvalidValue;
+    auto kern = o ? k_chunk_chain_cs<CS_OUT> : k_chunk_chain_cs<CS_PAIR>;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), cu, chunk_base, seq_order, (int)n_seq, total_tokens, H,
-                       initial_state, o, final_state, recs, vz);
+                       initial_state, o, final_state, recs, final_m);
     return hipGetLastError();
 }
 
@@ -1167,16 +1208,17 @@ hipError_t launch_chain(const void *q, const void *k, const void *v, const int32
 
 // ---------------------------------------------------------------------------
 // Chunk-level scan for few (sequence, head) pairs.  Over a segment of chunks
-// the state update is affine, S_out = S_in M + R ([GDN]'s recurrence is linear
-// in S with transitions g I - beta k k^T acting from the right).  Three
+// the state update is affine, S_out = S_in M + R (the gated delta rule is
+// linear in S, with transitions g I - beta k k^T acting from the right).  Two
 // column-split chain passes over all segments at once, and a short sequential
 // combine:
-//   A1  every segment from S = 0 with the real v       -> R_j (its final state)
-//   A2  every segment from S = I with v = 0            -> M_j (the product of its transitions)
+//   A   every segment, two states at once: from S = 0 with the real v -> R_j
+//       (its final state), and from S = I with v = 0 -> M_j (the product of
+//       its transitions)
 //   combine  per sequence over its segments j0 .. j0 + P_s - 1:
 //            S_in(j0) = S_0,  S_in(j+1) = S_in(j) M_j + R_j,  final state = S_in(j0 + P_s)
-//   D   every segment from S_in(j) with the real v     -> the outputs
-// The records of the per-chunk kernel serve all three passes unchanged.
+//   D   every segment from S_in(j) with the real v -> the outputs
+// The records of the per-chunk kernel serve both passes unchanged.
 
 // combine: one 8-wave workgroup per (sequence, head, block of 16 state rows);
 // the rows of S are independent.  Wave w forms the 16 x 16 tile of columns
@@ -1360,7 +1402,6 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
         segs.cu = reinterpret_cast<int32_t *>(ws + L.seg_cu_off);
         segs.base = reinterpret_cast<int32_t *>(ws + L.seg_base_off);
         segs.seg0 = reinterpret_cast<int32_t *>(ws + L.seg0_off);
-        segs.zero_page = reinterpret_cast<uint32_t *>(ws + L.zero_off);
         segs.P = sp.P;
         segs.n_seq = (int)n_seq;
         std::copy(sp.cu, sp.cu + sp.P + 1, segs.h_cu);
@@ -1381,16 +1422,12 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
         int32_t *seg_cu = reinterpret_cast<int32_t *>(ws + L.seg_cu_off);
         int32_t *seg_base = reinterpret_cast<int32_t *>(ws + L.seg_base_off);
         const int32_t *seg0 = reinterpret_cast<const int32_t *>(ws + L.seg0_off);
-        const uint16_t *zero_page = reinterpret_cast<const uint16_t *>(ws + L.zero_off);
         float *R = reinterpret_cast<float *>(ws + L.r_off), *M = reinterpret_cast<float *>(ws + L.m_off),
               *Sin = reinterpret_cast<float *>(ws + L.sin_off);
-        // A1 (the segment offsets and the zero page were written by k_chunk_prep)
-        if (e == hipSuccess)  // (A1 and A2 form states only)
+        // A: R_j and M_j in one pass (the segment offsets were written by k_chunk_prep)
+        if (e == hipSuccess)
             e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, nullptr, nullptr, R, recs,
-                                stream);
-        if (e == hipSuccess)  // A2
-            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, nullptr, nullptr, M, recs,
-                                stream, zero_page);
+                                stream, M);
         if (e == hipSuccess) {
             hipLaunchKernelGGL(k_scan_combine, dim3((unsigned)(64 * ((n_seq * H + 7) / 8))), dim3(512), 0, stream,
                                (int)n_seq, H, seg0, initial_state, R, M, Sin, final_state);
