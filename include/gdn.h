@@ -30,6 +30,14 @@
  *     finite q, k, v, beta and states; g <= 0 is treated as the smallest
  *     positive float by the chunked prefill.
  *   - Head dimensions: d_k == d_v, one of 16, 32, 64, 128.
+ *   - One kernel launch covers at most 2^32 - 1 work-items (the dispatch
+ *     packet's grid size is 32 bits); a call whose largest launch would
+ *     exceed that returns GDN_ERR_SHAPE.  The limits: chunked prefill
+ *     n_seq*H <= 2,097,144; token-serial prefill n_seq*H*max(1, d/32) <=
+ *     67,108,863; decode B*H <= 16,777,215 for d >= 64 and 67,108,863 below;
+ *     pre-processing 3 * ceil(H / (2048/d)) * ceil(total_tokens / R) <=
+ *     16,777,215 (R = 16 for bf16 and 8 for fp32 when the sequences average
+ *     at least R tokens, else 1).
  */
 #ifndef GDN_H
 #define GDN_H

@@ -200,6 +200,9 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
     if (!algo)
         return fail(GDN_ERR_UNSUPPORTED, "prefill: dtype=%d dk=%d dv=%d chunk=%d not supported", (int)dtype, dk, dv,
                     chunk);
+    if (is_chunked(algo) ? !gdn::prefill_chunked_fits(total_tokens, n_seq, H) : !gdn::prefill_serial_fits(dk, n_seq, H))
+        return fail(GDN_ERR_SHAPE, "prefill: n_seq=%lld total_tokens=%lld H=%d exceed one launch", (long long)n_seq,
+                    (long long)total_tokens, H);
     // sequence offsets
     if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr))
         return fail(GDN_ERR_NULL, "prefill: cu_seqlens and cu_seqlens_host must both be given or both be NULL");
@@ -275,6 +278,8 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtyp
     if (B < 0 || H <= 0 || B * (int64_t)H > (int64_t)UINT32_MAX)
         return fail(GDN_ERR_SHAPE, "decode_step: B=%lld H=%d", (long long)B, H);
     if (!supported_d(dk, dv)) return fail(GDN_ERR_UNSUPPORTED, "decode_step: dk=%d dv=%d not supported", dk, dv);
+    if (!gdn::decode_fits(dk, B * (int64_t)H))
+        return fail(GDN_ERR_SHAPE, "decode_step: B*H = %lld heads exceed one launch", (long long)(B * (int64_t)H));
     if (B == 0) return ok();
     if (!q || !k || !v || (!g && !(variant & GDN_VARIANT_NO_GATE)) || !beta || !state || !o)
         return fail(GDN_ERR_NULL, "decode_step: every pointer is required (g may be NULL without the gate)");
@@ -306,6 +311,9 @@ gdn_status gdn_decode_step_slots(const void *q, const void *k, const void *v, gd
                     (long long)n_slots);
     if (!supported_d(dk, dv))
         return fail(GDN_ERR_UNSUPPORTED, "decode_step_slots: dk=%d dv=%d not supported", dk, dv);
+    if (!gdn::decode_fits(dk, B * (int64_t)H))
+        return fail(GDN_ERR_SHAPE, "decode_step_slots: B*H = %lld heads exceed one launch",
+                    (long long)(B * (int64_t)H));
     if (B == 0) return ok();
     if (!q || !k || !v || (!g && !(variant & GDN_VARIANT_NO_GATE)) || !beta || !o || !slots)
         return fail(GDN_ERR_NULL, "decode_step_slots: q, k, v, g, beta, slots and o are required");
@@ -350,6 +358,9 @@ gdn_status gdn_preprocess(const void *xq, const void *xk, const void *xv, gdn_dt
         return fail(GDN_ERR_SHAPE, "preprocess: n_seq=%lld total_tokens=%lld H=%d", (long long)n_seq,
                     (long long)total_tokens, H);
     if (!supported_d(d, d)) return fail(GDN_ERR_UNSUPPORTED, "preprocess: d=%d not supported", d);
+    if (!gdn::preprocess_fits(dtype == GDN_BF16, d, n_seq, total_tokens, H))
+        return fail(GDN_ERR_SHAPE, "preprocess: n_seq=%lld total_tokens=%lld H=%d exceed one launch",
+                    (long long)n_seq, (long long)total_tokens, H);
     if (activation != GDN_ACT_NONE && activation != GDN_ACT_SILU)
         return fail(GDN_ERR_UNSUPPORTED, "preprocess: activation %d", activation);
     if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr))

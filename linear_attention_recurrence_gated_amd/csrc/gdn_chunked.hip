@@ -1360,6 +1360,15 @@ size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int 
     return ws_layout(total_tokens, n_seq, H, scan_possible(mode, n_seq, H)).total;
 }
 
+// The largest launches: the column-split chain (CS_TILES workgroups of 512
+// per (sequence, head), rounded up to groups of 8 pairs; the other chain forms
+// launch fewer work-items) and k_chunk_prep (one workgroup of 256 per (chunk, head)).
+bool prefill_chunked_fits(int64_t total_tokens, int64_t n_seq, int H) {
+    const int64_t units8 = (n_seq * H + 7) / 8 * 8;
+    const int64_t chunks = (total_tokens + C - 1) / C + n_seq;  // at least the sum over sequences
+    return launch_fits(units8 * CS_TILES, 512) && launch_fits(chunks * H, 256);
+}
+
 bool prefill_chunked_scan_supported(int64_t n_seq, int64_t total_tokens) {
     return n_seq >= 1 && n_seq <= SCAN_MAX_SEGMENTS && total_tokens > 0;
 }
@@ -1369,6 +1378,7 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
                                   int64_t total_tokens, int H, const float *initial_state, float *o,
                                   float *final_state, void *workspace, int erase, int mode,
                                   const hipEvent_t *marks, hipStream_t stream) {
+    if (!prefill_chunked_fits(total_tokens, n_seq, H)) return hipErrorInvalidConfiguration;
     const WsLayout L = ws_layout(total_tokens, n_seq, H, scan_possible(mode, n_seq, H));
     ScanPlan sp;
     if (L.scan_cap > 0 && plan_scan(cu_seqlens_host, n_seq, total_tokens, H, mode == CHUNKED_SCAN, sp) &&

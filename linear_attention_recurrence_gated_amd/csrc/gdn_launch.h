@@ -9,6 +9,18 @@
 
 namespace gdn {
 
+// One launch covers at most 2^32 - 1 work-items (the dispatch packet's grid
+// size is a 32-bit count of work-items).
+inline bool launch_fits(int64_t blocks, int64_t threads) {
+    return blocks >= 0 && blocks <= (int64_t)0xFFFFFFFFLL / threads;
+}
+// Whether every kernel of a call fits one launch (checked by the API before
+// anything is enqueued).
+bool decode_fits(int d, int64_t BH);
+bool prefill_serial_fits(int d, int64_t n_seq, int H);
+bool prefill_chunked_fits(int64_t total_tokens, int64_t n_seq, int H);
+bool preprocess_fits(bool bf16, int d, int64_t n_seq, int64_t total_tokens, int H);
+
 // One decode step for B*H heads (in-place state update).
 hipError_t launch_decode(bool bf16, int d, const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, float *o, int64_t BH, int H, const int32_t *slots,

@@ -30,11 +30,12 @@
 // The returned conv state (the last three raw inputs of each sequence) is
 // written by k_preprocess itself, by the thread at the sequence's last token,
 // from its window, when that is safe (see fuse_conv_state); otherwise by
-// k_conv_state: one thread per (sequence, tensor, head, channel) copies the
+// k_conv_state: one thread per (sequence, tensor, head, channel), grid-stride, copies the
 // sequence's last three raw inputs (shifting in the starting state for a
 // sequence shorter than three) to the returned conv state.  It reads all
 // three values before writing any, so the returned state may be the starting
 // state itself; it runs after k_preprocess has read the starting state.
+#include <algorithm>
 #include <cfloat>
 
 #include "gdn_device.h"
@@ -253,13 +254,10 @@ __global__ __launch_bounds__(256) void k_preprocess(const TIn *__restrict__ xq, 
 }
 
 template <typename TIn>
-__global__ __launch_bounds__(256) void k_conv_state(const TIn *__restrict__ xq, const TIn *__restrict__ xk,
-                                                    const TIn *__restrict__ xv, const TIn *st_in, TIn *st_out,
-                                                    const int32_t *__restrict__ cu, int64_t n_seq,
-                                                    int64_t total_tokens, int H, int D) {
-    const int64_t per_seq = 3LL * H * D;  // (tensor, head, channel) per sequence
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= n_seq * per_seq) return;
+__device__ __forceinline__ void conv_state_one(const TIn *__restrict__ xq, const TIn *__restrict__ xk,
+                                               const TIn *__restrict__ xv, const TIn *st_in, TIn *st_out,
+                                               const int32_t *__restrict__ cu, int64_t total_tokens, int H, int D,
+                                               int64_t per_seq, int64_t idx) {
     const int64_t s = idx / per_seq, rem = idx % per_seq;
     const int tau = (int)(rem / ((int64_t)H * D));
     const int64_t hc = rem % ((int64_t)H * D);
@@ -282,6 +280,34 @@ __global__ __launch_bounds__(256) void k_conv_state(const TIn *__restrict__ xq, 
     for (int i = 0; i < 3; ++i) st_out[((s * 3 + tau) * 3 + i) * H * D + hc] = vals[i];
 }
 
+template <typename TIn>
+__global__ __launch_bounds__(256) void k_conv_state(const TIn *__restrict__ xq, const TIn *__restrict__ xk,
+                                                    const TIn *__restrict__ xv, const TIn *st_in, TIn *st_out,
+                                                    const int32_t *__restrict__ cu, int64_t n_seq,
+                                                    int64_t total_tokens, int H, int D) {
+    const int64_t per_seq = 3LL * H * D;  // (tensor, head, channel) per sequence
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n_seq * per_seq;
+         idx += (int64_t)gridDim.x * 256)
+        conv_state_one(xq, xk, xv, st_in, st_out, cu, total_tokens, H, D, per_seq, idx);
+}
+
+#ifndef GDN_PRE_RANGE_BF16
+#define GDN_PRE_RANGE_BF16 16
+#endif
+// Tokens per range of the long-sequence form: 16 rows of bf16 or 8 of fp32,
+// 64 VGPRs in flight either way.
+constexpr int range_long(bool bf16) { return bf16 ? GDN_PRE_RANGE_BF16 : 8; }
+// Ranges of range_long tokens pay off when sequences are longer than a range;
+// batches of shorter ones (decode steps) take one token per range.
+int pre_range(bool bf16, int64_t n_seq, int64_t N) {
+    return N >= (int64_t)range_long(bf16) * n_seq ? range_long(bf16) : 1;
+}
+// Workgroups of one k_preprocess launch: (tensor, group of 2048/d heads, range).
+int64_t pre_blocks(int d, int R, int64_t N, int H) {
+    const int hpb = 2048 / d;
+    return 3LL * ((H + hpb - 1) / hpb) * ((N + R - 1) / R);
+}
+
 template <typename TIn, int D, int R>
 hipError_t launch_pre_kernel(const void *xq, const void *xk, const void *xv, const float *w, const void *st_in,
                              const float *a, const float *b, const float *bias, const int32_t *cu, int64_t n_seq,
@@ -291,7 +317,7 @@ hipError_t launch_pre_kernel(const void *xq, const void *xk, const void *xv, con
     const int n_hg = (H + HPB - 1) / HPB;
     const int64_t n_ranges = (N + R - 1) / R;
     const int64_t blocks = 3LL * n_hg * n_ranges;
-    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    if (blocks != pre_blocks(D, R, N, H) || !launch_fits(blocks, 256)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((k_preprocess<TIn, D, R>), dim3((unsigned)blocks), dim3(256), 0, stream, (const TIn *)xq,
                        (const TIn *)xk, (const TIn *)xv, w, (const TIn *)st_in, a, b, bias, cu, (int)n_seq, N, H, act,
                        n_hg, (uint32_t)n_ranges, (TIn *)q, (TIn *)k, (TIn *)v, g, beta, (TIn *)st_out_fused);
@@ -317,13 +343,8 @@ hipError_t preprocess_d(const void *xq, const void *xk, const void *xv, const fl
                         void *st_out, const float *a, const float *b, const float *bias, const int32_t *cu,
                         const int32_t *cu_host, int64_t n_seq, int64_t N, int H, int act, void *q, void *k, void *v,
                         float *g, float *beta, hipStream_t stream) {
-#ifndef GDN_PRE_RANGE_BF16
-#define GDN_PRE_RANGE_BF16 16
-#endif
-    // tokens per range: 16 rows of bf16 or 8 of fp32, 64 VGPRs in flight either way
-    constexpr int R_LONG = sizeof(TIn) == 2 ? GDN_PRE_RANGE_BF16 : 8;
-    // ranges of R_LONG tokens pay off when sequences are longer than a range
-    const bool long_seqs = N >= (int64_t)R_LONG * n_seq;
+    constexpr int R_LONG = range_long(sizeof(TIn) == 2);
+    const bool long_seqs = pre_range(sizeof(TIn) == 2, n_seq, N) == R_LONG;
     const bool fused = N > 0 && fuse_conv_state(cu_host, n_seq, N, long_seqs ? R_LONG : 1, st_in && st_in == st_out);
     if (N > 0) {
         void *so = fused ? st_out : nullptr;
@@ -336,7 +357,8 @@ hipError_t preprocess_d(const void *xq, const void *xk, const void *xv, const fl
     }
     const int64_t n = n_seq * 3LL * H * D;
     if (n > 0 && !fused) {
-        hipLaunchKernelGGL((k_conv_state<TIn>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+        hipLaunchKernelGGL((k_conv_state<TIn>), dim3((unsigned)std::min<int64_t>((n + 255) / 256, 65536)), dim3(256),
+                           0, stream,
                            (const TIn *)xq, (const TIn *)xk, (const TIn *)xv, (const TIn *)st_in, (TIn *)st_out, cu,
                            n_seq, N, H, D);
         return hipGetLastError();
@@ -345,6 +367,10 @@ hipError_t preprocess_d(const void *xq, const void *xk, const void *xv, const fl
 }
 
 }  // namespace
+
+bool preprocess_fits(bool bf16, int d, int64_t n_seq, int64_t total_tokens, int H) {
+    return d >= 8 && launch_fits(pre_blocks(d, pre_range(bf16, n_seq, total_tokens), total_tokens, H), 256);
+}
 
 hipError_t launch_preprocess(bool bf16, int d, const void *xq, const void *xk, const void *xv, const float *w,
                              const void *st_in, void *st_out, const float *a_logit, const float *b_logit,

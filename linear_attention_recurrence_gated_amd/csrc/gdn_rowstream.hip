@@ -193,11 +193,19 @@ __global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q
 // accesses and may stay cache-resident from one step to the next.
 constexpr int64_t DECODE_NT_MIN_BYTES = int64_t(32) << 20;
 
+// waves per decode workgroup; row tiles (workgroups) per (sequence, head) of the serial prefill
+static constexpr int decode_waves(int d) { return d >= 64 ? 4 : 1; }
+static constexpr int serial_tiles(int d) { return d >= 32 ? d / 32 : 1; }
+
+bool decode_fits(int d, int64_t BH) { return launch_fits(BH, 64 * decode_waves(d)); }
+bool prefill_serial_fits(int d, int64_t n_seq, int H) { return launch_fits(n_seq * H * serial_tiles(d), 64); }
+
 template <typename TIn, int D>
 static hipError_t decode_d(const void *q, const void *k, const void *v, const float *g, const float *beta,
                            float *state, float *o, int64_t BH, int H, const int32_t *slots, int64_t n_slots,
                            int erase, hipStream_t stream) {
-    constexpr int NW = D >= 64 ? 4 : 1;
+    constexpr int NW = decode_waves(D);
+    if (!decode_fits(D, BH)) return hipErrorInvalidConfiguration;
     if (BH * D * D * 4 >= DECODE_NT_MIN_BYTES)
         hipLaunchKernelGGL((k_decode_step<TIn, D, NW, true>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
                            (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o, slots, n_slots, H,
@@ -232,7 +240,9 @@ static hipError_t serial_d(const void *q, const void *k, const void *v, const fl
                            const int32_t *cu, int64_t n_seq, int64_t total, int H, const float *s_in, float *o,
                            float *s_out, int erase, hipStream_t stream) {
     constexpr int ROWS = D >= 32 ? 32 : D;
+    static_assert(D / ROWS == serial_tiles(D), "row tiles per (sequence, head)");
     const int64_t blocks = n_seq * H * (D / ROWS);
+    if (!launch_fits(blocks, 64)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((k_prefill_serial<TIn, D, ROWS>), dim3((unsigned)blocks), dim3(64), 0, stream,
                        (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, cu, total, H, s_in, o, s_out, erase);
     return hipGetLastError();

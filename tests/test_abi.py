@@ -298,3 +298,36 @@ def test_scan_mode_validation():
     assert ws(65, 1, gdn.CHUNK_64) == ws(65, 1, gdn.CHUNK_64_CHAIN)
     assert ws(1, 4, gdn.CHUNK_64_SCAN) > \
         gdn.prefill_workspace_bytes(4096, 1, 4, 128, 128, gdn.GDN_BF16, gdn.CHUNK_64_CHAIN)
+
+
+def test_launch_size_limits():
+    """A call whose kernels would exceed 2^32 - 1 work-items in one launch is
+    rejected (GDN_ERR_SHAPE) before anything is enqueued; one size below each
+    limit passes the check (and fails later on the fake pointers instead)."""
+    # chunked prefill: 4 column-split workgroups of 512 per (sequence, head), in groups of 8 pairs
+    kw = dict(dk=128, dv=128, chunk=gdn.CHUNK_64, N=40000)
+    st, msg = _prefill(n_seq=2097152 // 64 + 1, H=64, **kw)
+    assert st == 2 and "exceed one launch" in msg, (st, msg)
+    st, msg = _prefill(n_seq=2097144 // 8, H=8, **kw)
+    assert st == 5, (st, msg)  # past the size check: no cu_seqlens for several sequences
+    # token-serial prefill at d = 128: 4 workgroups of 64 per (sequence, head)
+    kw = dict(dk=128, dv=128, dtype=gdn.GDN_FP32, chunk=gdn.CHUNK_SERIAL, N=64)
+    st, msg = _prefill(n_seq=(1 << 24) // 16, H=16, **kw)
+    assert st == 2 and "exceed one launch" in msg, (st, msg)
+    st, msg = _prefill(n_seq=(1 << 24) // 16 - 1, H=16, **kw)
+    assert st == 5, (st, msg)
+
+    L = gdn.lib()
+
+    def decode(B, H):
+        L.gdn_last_error()
+        return L.gdn_decode_step(FAKE, FAKE, FAKE, gdn.GDN_BF16, FAKE, FAKE, FAKE * 64, FAKE * 128, B, H, 128, 128,
+                                 0, None)
+
+    assert decode(1 << 23, 2) == 2       # 2^24 heads of 256 work-items
+    assert decode((1 << 23) - 1, 2) == 8  # past the size check: o overlaps q
+    # pre-processing, d = 128 bf16: 3 tensors x ceil(H/16) head groups x ceil(N/16) ranges, 256 work-items each
+    st, msg = _preprocess(N=16 * ((1 << 24) // 3 + 1), H=16, d=128)
+    assert st == 2 and "exceed one launch" in msg, (st, msg)
+    st, msg = _preprocess(N=16 * ((1 << 24) // 3), H=16, d=128)
+    assert st != 2, (st, msg)
