@@ -75,7 +75,7 @@ def source_hash(kernel):
 
 def load_traffic(kernel):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/), if the
-    kernel's sources still match the build the counters were taken on."""
+    kernel's sources still match those the counters were taken on."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -396,7 +396,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the recurrence shards across heads and sequences with no "
-              "exchange, so multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+              "exchange, so each GPU runs its own share independently (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch

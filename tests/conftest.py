@@ -12,7 +12,7 @@ if HERE not in sys.path:
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs on the GPU box")
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
 
 
 @pytest.fixture(scope="session")
