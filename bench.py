@@ -117,6 +117,28 @@ def time_block(torch, fn, steps):
     return a.elapsed_time(b) / steps, time.perf_counter() - t0
 
 
+# After an idle spell the GPU's clocks take tens of milliseconds of continuous
+# work to settle: measured on the prefill, the first 10 ms of back-to-back
+# calls ran at 197 us per call, the next at 181, then 172-173 from about 20 ms
+# on.  Each measurement below is therefore preceded by SPIN_UP_S seconds of
+# the same untimed calls (on top of the warm-up steps), so that it reports the
+# steady state that a model running layer after layer sees.
+SPIN_UP_S = 0.15
+
+
+def spin_up(torch, fn, seconds=SPIN_UP_S):
+    """Untimed calls fn(0), fn(1), ... in batches of 16 until `seconds` of
+    wall time have passed; returns the number of calls."""
+    torch.cuda.synchronize()
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
 def time_each(torch, fn, steps):
     """Sorted ms of `steps` calls fn(i), each bracketed by its own pair of
     events (for percentiles; includes the events' own idle time)."""
@@ -157,6 +179,7 @@ def bench_prefill(torch, gdn, w, steps, warmup, rotate):
     def step(i):
         call(sets[i % rotate])
 
+    spin_up(torch, step)
     for i in range(warmup):
         step(i)
     block_ms, wall = time_block(torch, step, steps)
@@ -201,6 +224,8 @@ def bench_decode(torch, gdn, w, steps, rotate):
         gdn.decode_step(q[t], k[t], v[t], g[t], beta[t], states[t % rotate], out=o[t])
 
     init()
+    spin_up(torch, lambda t: step(t % steps))
+    init()
     for t in range(steps):  # warm-up pass
         step(t)
     init()
@@ -230,6 +255,7 @@ def bench_scan(torch, gdn, w, steps, warmup):
             ws = torch.empty(gdn.prefill_workspace_bytes(T_, 1, 6, D, D, gdn.GDN_BF16, ch), dtype=torch.uint8,
                              device=dev)
             call = lambda: gdn.prefill(q, k, v, g, beta, chunk=ch, out=o, final_state=st, workspace=ws)
+            spin_up(torch, lambda i: call())
             for _ in range(warmup):
                 call()
             row[name + "_ms"], _ = time_block(torch, lambda i: call(), steps)
@@ -263,8 +289,7 @@ def bench_decode_slots(torch, gdn, w, steps, rotate):
         gdn.decode_step_slots(q, k, v, g, beta, pool, slots, slots_host=None, out=o)
 
     def timed(fns):
-        for f in fns:
-            f()
+        spin_up(torch, lambda t: fns[t % len(fns)]())
         fn = lambda t: fns[t % len(fns)]()
         return time_block(torch, fn, steps)[0], time_each(torch, fn, steps)
 
@@ -274,7 +299,7 @@ def bench_decode_slots(torch, gdn, w, steps, rotate):
         for pool in pools:
             step(pool)
     replays = max(1, steps // len(pools))
-    gr.replay()
+    spin_up(torch, lambda t: gr.replay())
     blk, _ = time_block(torch, lambda t: gr.replay(), replays)
     each = time_each(torch, lambda t: gr.replay(), replays)
     return eager, (blk / len(pools), [x / len(pools) for x in each])
@@ -301,6 +326,7 @@ def bench_preprocess(torch, gdn, w, steps, warmup, rotate):
         gdn.preprocess(s["xq"], s["xk"], s["xv"], wt, s["a"], s["b"], gate_bias=bias, conv_state_in=s["st"],
                        conv_state_out=st_out[i % rotate], activation="silu", out=outs[i % rotate])
 
+    spin_up(torch, call)
     for i in range(warmup):
         call(i)
     return time_block(torch, call, steps)[0], time_each(torch, call, steps)
@@ -467,6 +493,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spin_up_s": SPIN_UP_S,
         "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
