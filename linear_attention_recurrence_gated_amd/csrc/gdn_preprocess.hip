@@ -23,9 +23,10 @@
 // each output byte written once; per token a workgroup reads and writes one
 // contiguous run of heads.  The squared norm of a (token, head) is a DPP sum
 // over its D/8 lanes.  Workgroups of the v tensor also map the gates of their
-// (token, head) block.  Workgroup indices are remapped so that each XCD takes
-// a contiguous run of token ranges (neighbouring ranges share window rows in
-// that XCD's L2).  Batches of short sequences (decode steps) use R = 1.
+// (token, head) block.  Consecutive workgroups take consecutive token ranges
+// (mapping each XCD a contiguous run instead, so that neighbouring ranges
+// share window rows in its L2, measured 2% slower).  Batches of short
+// sequences (decode steps) use R = 1.
 //
 // The returned conv state (the last three raw inputs of each sequence) is
 // written by k_preprocess itself, by the thread at the sequence's last token,
@@ -106,11 +107,6 @@ __device__ __forceinline__ int seq_of(const int32_t *cu, int n_seq, int64_t t) {
     return lo;
 }
 
-// Block b is dispatched to XCD b % 8; give XCD x the contiguous logical
-// indices [x n/8, (x+1) n/8) when n is a multiple of 8.
-__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t n) {
-    return (n & 7u) ? b : (b & 7u) * (n >> 3) + (b >> 3);
-}
 
 // One token of one (tensor, head) row slice: convolution over the window
 // w0..w2 (oldest first) and the current input, activation, norm, store.
@@ -150,7 +146,7 @@ __global__ __launch_bounds__(256) void k_preprocess(const TIn *__restrict__ xq, 
     using V = Vec8<TIn>;
     constexpr int LPR = D / 8;      // lanes per head
     constexpr int HPB = 256 / LPR;  // heads per workgroup
-    const uint32_t L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const uint32_t L = blockIdx.x;
     const uint32_t r = L % n_ranges, rest = L / n_ranges;
     const int hg = (int)(rest % (uint32_t)n_hg), tau = (int)(rest / (uint32_t)n_hg);
     const int lr = threadIdx.x % LPR;
