@@ -1174,16 +1174,16 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     }
 }
 
-// o != NULL: the outputs and final states (CS_OUT); o == NULL: the pair of
-// states into final_state and final_m (CS_PAIR).
+// final_m == NULL: the outputs and final states (CS_OUT; o is NULL only in a
+// batch without tokens, when nothing is stored to it); final_m != NULL: the
+// pair of states into final_state and final_m (CS_PAIR; o is not used).
 hipError_t launch_chain_cs(const void *q, const void *k, const void *v, const int32_t *cu, const int32_t *chunk_base,
                            const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H,
                            const float *initial_state, float *o, float *final_state, const char *recs,
                            hipStream_t stream, float *final_m = nullptr) {
     const int64_t units = n_seq * H;
     const int64_t grid = ((units + 7) / 8) * 8 * CS_TILES;
-    if (!o && !final_m) return hipErrorInvalidValue;
-    auto kern = o ? k_chunk_chain_cs<CS_OUT> : k_chunk_chain_cs<CS_PAIR>;
+    auto kern = final_m ? k_chunk_chain_cs<CS_PAIR> : k_chunk_chain_cs<CS_OUT>;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), cu, chunk_base, seq_order, (int)n_seq, total_tokens, H,

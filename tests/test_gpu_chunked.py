@@ -225,3 +225,22 @@ def test_config4_segments_equal_one_shot(oracle_lib):
     es = rel_max_err(s_h, s_ref)
     say(f"config4 vs oracle (sampled heads): o={eo:.2e} state={es:.2e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("chunk", [gdn.CHUNK_64, gdn.CHUNK_64_CHAIN, gdn.CHUNK_SERIAL])
+def test_batch_without_tokens(oracle_lib, chunk):
+    """Three empty sequences: no output rows, and every final state equals its
+    initial state (zero-length sequences copy their state); the oracle agrees."""
+    say("prefill with no tokens, chunk", chunk)
+    inp = w.make_prefill([0, 0, 0], H=3, d=128, seed=13, init_std=0.2)
+    o, s = gpu_prefill(inp, chunk=chunk)
+    o_ref, s_ref = oracle_prefill(inp)
+    assert o.shape == (0, 3, 128) and o_ref.shape[0] == 0
+    assert np.array_equal(s, inp.s_init) and np.array_equal(s_ref, inp.s_init)
+
+
+def test_scan_refuses_a_batch_without_tokens():
+    inp = w.make_prefill([0, 0], H=2, d=128, seed=14, init_std=0.2)
+    with pytest.raises(gdn.GdnError) as e:
+        gpu_prefill(inp, chunk=gdn.CHUNK_64_SCAN)
+    assert e.value.name == "GDN_ERR_UNSUPPORTED"

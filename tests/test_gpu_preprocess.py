@@ -199,3 +199,14 @@ def test_feeds_the_recurrence(oracle_lib):
     eo, es = rel_max_err(host(o), o_ref), rel_max_err(host(s), s_ref)
     say(f"  errors o={eo:.2e} state={es:.2e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_batch_without_tokens(oracle_lib):
+    """Two empty sequences: no rows to compute; the returned conv state is the
+    starting state, bit for bit (the oracle's as well)."""
+    say("preprocess with no tokens")
+    inp = w.make_preprocess([0, 0], H=4, d=64, dtype="bf16", seed=95, activation="silu")
+    res = run_gpu(inp)
+    ref = run_oracle(inp)
+    assert res[0].shape[0] == 0 and res[3].shape[0] == 0
+    assert np.array_equal(host(res[5]), ref[5]) and np.array_equal(ref[5], inp.state_in.astype(np.float64))
