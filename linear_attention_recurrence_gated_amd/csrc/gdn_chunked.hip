@@ -13,26 +13,34 @@
 //   outputs        O = diag(e^{G_t}) Q S0^T + P U,   P[t][s] = beta_s e^{G_t - G_s} (q_t . k_s), s <= t
 //   next state     S = e^{G_n} S0 + (diag(beta_t e^{G_n - G_t}) U)^T K
 //
+// With Y = V - diag(e^{G_{t-1}}) K S0^T (so U = T Y), the kernels use the
+// equivalent products
+//   outputs        O = diag(e^{G_t}) Q S0^T + (P T) Y
+//   next state     S^T = e^{G_n} S0^T + K^T (Tw Y),   Tw = diag(beta_t e^{G_n - G_t}) T
+// so that U itself is never formed: P T and Tw are per-chunk constants.
+//
 // Every exponent is a difference G_a - G_b with a >= b, never positive for
 // g <= 1, so nothing overflows however strong the decay.  T and P depend only
 // on the chunk's own keys, queries and gates; everything that touches the
 // state is in the last three lines.  In a partial chunk the rows past the end
 // are copies of the last row with beta = 0 and lambda = 0; T and P are lower
-// triangular and beta = 0 zeroes their columns, so those rows never reach a
-// real row, and beta = 0 keeps them out of the next state.
+// triangular and beta = 0 zeroes their columns (and T's column s is then the
+// unit vector, so P T's column s is P's, zero), so those rows never reach a
+// real row, and beta = 0 zeroes their rows of Tw, keeping them out of the
+// next state.
 //
 // Kernels (bf16 q/k/v, d_k = d_v = 128, fp32 gates, state and outputs):
 //   k_plan         varlen only: per-sequence chunk offsets and a longest-first order.
 //   k_chunk_prep   one 4-wave workgroup per (chunk, head), all in parallel:
-//                  K K^T and Q K^T on MFMA, the masked L and P, and
-//                  T = (I + L)^{-1} by 16x16 blocks.  It writes a 25 KiB record
-//                  per (chunk, head): T and P as split bf16 MFMA fragments and
-//                  the gate factors e^{G_t}, beta_t e^{G_n - G_t}, e^{G_n},
-//                  e^{G_{t-1}}.
-//   k_chunk_chain  one workgroup per (sequence, head, 16*NW rows of S), walking
-//                  the sequence's chunks with S^T in MFMA accumulators.  NW
+//                  K K^T and Q K^T on MFMA, the masked L and P,
+//                  T = (I + L)^{-1} by 16x16 blocks, and P T.  It writes a
+//                  25 KiB record per (chunk, head): Tw and P T as split bf16
+//                  MFMA fragments and the gate factors e^{G_t}, e^{G_{t-1}},
+//                  e^{G_n}.
+//   k_chunk_chain  one workgroup per (sequence, head, 64 rows of S), walking
+//                  the sequence's chunks with S^T in MFMA accumulators.  Four
 //                  copy waves stream the record and the q, k, v rows of the
-//                  next chunk into LDS with direct global->LDS loads while NW
+//                  next chunk into LDS with direct global->LDS loads while four
 //                  compute waves work on the current chunk (double buffer, one
 //                  barrier per chunk).  Each compute wave owns 16 rows of S:
 //                  rows are independent, so the waves and workgroups of one
@@ -53,7 +61,6 @@
 // transposes 16-bit elements across each group of 16 lanes.
 #include <algorithm>
 #include <cfloat>
-#include <cstdlib>
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -73,17 +80,19 @@ constexpr int T_BLOCKS = 6;
 // One record per (chunk, head) in the workspace, copied verbatim into LDS by
 // the chain kernel.  Fragments of a lower-triangular 64x64 matrix are the
 // T_BLOCKS nonzero 16x32 blocks tblk(tb, ks), each split into hi and lo bf16.
-constexpr int FRAG = 1024;                            // 64 lanes x 16 bytes
-constexpr int REC_T_HI = 0;                           // T = (I + L)^{-1}
-constexpr int REC_T_LO = REC_T_HI + T_BLOCKS * FRAG;
-constexpr int REC_P_HI = REC_T_LO + T_BLOCKS * FRAG;  // P
-constexpr int REC_P_LO = REC_P_HI + T_BLOCKS * FRAG;
-constexpr int REC_GATE = REC_P_LO + T_BLOCKS * FRAG;  // floats, below
-constexpr int GATE_EG = 0;                            // e^{G_t}, t = 0..63
-constexpr int GATE_BW = 64;                           // beta_t e^{G_n - G_t}
-constexpr int GATE_EGN = 128;                         // e^{G_n}
-constexpr int GATE_EGM1 = 192;                        // e^{G_{t-1}}
-constexpr int REC_BYTES = REC_GATE + FRAG;            // 25 KiB
+// The chain needs T only as diag(beta_t e^{G_n - G_t}) T (the state update
+// takes U only in that row scaling) and P only as P T (the outputs are
+// P U = (P T) Y), so the record holds those two products.
+constexpr int FRAG = 1024;                              // 64 lanes x 16 bytes
+constexpr int REC_TW_HI = 0;                            // Tw = diag(beta_t e^{G_n - G_t}) T
+constexpr int REC_TW_LO = REC_TW_HI + T_BLOCKS * FRAG;
+constexpr int REC_PT_HI = REC_TW_LO + T_BLOCKS * FRAG;  // PT = P T
+constexpr int REC_PT_LO = REC_PT_HI + T_BLOCKS * FRAG;
+constexpr int REC_GATE = REC_PT_LO + T_BLOCKS * FRAG;   // floats, below
+constexpr int GATE_EG = 0;                              // e^{G_t}, t = 0..63
+constexpr int GATE_EGM1 = 64;                           // e^{G_{t-1}}
+constexpr int GATE_EGN = 128;                           // e^{G_n}
+constexpr int REC_BYTES = REC_GATE + FRAG;              // 25 KiB
 constexpr int REC_PIECES = REC_BYTES / FRAG;
 static_assert(REC_BYTES % 256 == 0, "record layout");
 
@@ -421,7 +430,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
     dma_rows(S.KL, k + cbase, rs, n, lane, wave, 4);
     dma_rows(S.QT, q + cbase, rs, n, lane, wave, 4);
     asm volatile("" : "+v"(gl), "+v"(bl));  // keeps the gate arithmetic after the copies are issued
-    float f_eg = 0.f, f_bw = 0.f, f_egm1 = 0.f, f_egn = 0.f;  // the record's gate factors (wave 0)
+    float f_eg = 0.f, f_egm1 = 0.f, f_egn = 0.f;  // the record's gate factors (wave 0)
     if (wave == 0) {  // gate prefix sums
         const float lam = (lane < n && g) ? __logf(fmaxf(gl, FLT_MIN)) : 0.f;
         const float bt = lane < n ? bl : 0.f;
@@ -431,9 +440,8 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
         S.G[lane] = G;
         S.B[lane] = bt;
         f_eg = __expf(G);
-        f_bw = bt * __expf(G63 - G);
         // without the erase term nothing is recalled from the entering state:
-        // Y = V - 0 X = V, and L = 0 below makes T = I, so U = V
+        // Y = V - 0 X = V, and L = 0 below makes T = I
         f_egm1 = !erase ? 0.f : lane > 0 ? __expf(Gm1) : 1.f;
         f_egn = __expf(G63);
     }
@@ -442,15 +450,16 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
     if (wave == 0) {  // stored after the barrier: nothing waits for these writes
         float *gate = reinterpret_cast<float *>(rec + REC_GATE);
         gate[GATE_EG + lane] = f_eg;
-        gate[GATE_BW + lane] = f_bw;
         gate[GATE_EGM1 + lane] = f_egm1;
         if (lane == 63) gate[GATE_EGN] = f_egn;
     }
 
     // K K^T tiles (the 10 tiles on and below the diagonal; item i = wave + 4 j,
-    // i < 10, kept in registers until k's tile may be overwritten) and the P
-    // fragments (items 10..15, straight to the record).
-    f32x4_t Lr[3];
+    // i < 10, kept in registers until k's tile may be overwritten) and the
+    // blocks of P (items 10..15: block i - 10, its two 16x16 halves kept in
+    // registers as fp32 until P T is formed).  Lane (g, r) of a P half holds
+    // P[16 tb + r][16 sa + 4 g + e].
+    f32x4_t Lr[3], Pr[2][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int i = wave + 4 * j;
@@ -471,9 +480,8 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
             }
             if (j < 3) Lr[j] = acc;
         } else if (i < 16) {
-            const int pb = i - 10;  // P fragment tblk(tb, ks)
+            const int pb = i - 10;
             const int tb = pb < 2 ? pb : 2 + ((pb - 2) >> 1), ks = pb < 2 ? 0 : ((pb - 2) & 1);
-            u32x2_t hi[2], lo[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int sa = 2 * ks + half;
@@ -491,12 +499,8 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
                         p[e] = sx <= t ? S.B[sx] * __expf(Gt - S.G[sx]) * acc[e] : 0.f;
                     }
                 }
-                split4(p, hi[half], lo[half]);
+                if (j >= 2) Pr[j - 2][half] = p;
             }
-            *reinterpret_cast<u32x4_t *>(rec + REC_P_HI + pb * FRAG + lane * 16) =
-                u32x4_t{hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
-            *reinterpret_cast<u32x4_t *>(rec + REC_P_LO + pb * FRAG + lane * 16) =
-                u32x4_t{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
         }
     }
     lds_barrier();  // k and q are no longer needed: their tiles become L and T
@@ -548,6 +552,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
     //   T10 = -D1 (L10 D0),  T32 = -D3 (L32 D2)                  (waves 0, 1)
     //   Z   = L[32:64][0:32] T_A                                  (4 waves, one 16x16 tile each)
     //   T[32:64][0:32] = -T_B Z                                   (4 waves)
+    // (The top-right 32x32 part of the tile is never written nor read.)
     {
         float *scr = S.scr;  // M: [2][16][16], then Z: [32][36]
         if (wave < 2) {
@@ -587,20 +592,99 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
 #pragma unroll
             for (int e = 0; e < 4; ++e) *tref(S.QT, 32 + 16 * ti + 4 * g4 + e, 16 * tj + r) = -t[e];
         }
-        lds_barrier();
+        lds_barrier();  // T complete; L no longer needed
     }
 
-    // T fragments: block tblk(tb, ks), lane (g, r) holds T[16 tb + r][32 ks + slot_k(g, e)], split hi/lo
+    // P (fp32) into the L tile, for the product P T
+#pragma unroll
+    for (int j = 2; j < 4; ++j) {
+        const int i = wave + 4 * j;
+        if (i >= 10 && i < 16) {
+            const int pb = i - 10;
+            const int tb = pb < 2 ? pb : 2 + ((pb - 2) >> 1), ks = pb < 2 ? 0 : ((pb - 2) & 1);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int sa = 2 * ks + half;
+                if (sa <= tb) {
+                    const f32x4_t p = Pr[j - 2][half];
+                    *reinterpret_cast<float4 *>(tref(S.KL, 16 * tb + r, 16 * sa + 4 * g4)) =
+                        make_float4(p[0], p[1], p[2], p[3]);
+                }
+            }
+        }
+    }
+    // Tw fragments: block tblk(tb, ks), lane (g, r) holds
+    // beta_t e^{G_n - G_t} T[t][32 ks + slot_k(g, e)], t = 16 tb + r, split hi/lo
     for (int pb = wave; pb < T_BLOCKS; pb += 4) {
         const int tb = pb < 2 ? pb : 2 + ((pb - 2) >> 1), ks = pb < 2 ? 0 : ((pb - 2) & 1);
-        const float4 a = t4(S.QT, 16 * tb + r, 32 * ks + 4 * g4);
-        const float4 b = t4(S.QT, 16 * tb + r, 32 * ks + 16 + 4 * g4);
-        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const int t = 16 * tb + r;
+        const float bw = S.B[t] * __expf(S.G[63] - S.G[t]);
+        const float4 a = t4(S.QT, t, 32 * ks + 4 * g4);
+        const float4 b = t4(S.QT, t, 32 * ks + 16 + 4 * g4);
+        const float x[8] = {bw * a.x, bw * a.y, bw * a.z, bw * a.w, bw * b.x, bw * b.y, bw * b.z, bw * b.w};
         u32x4_t hi, lo;
         split8(x, hi, lo);
-        *reinterpret_cast<u32x4_t *>(rec + REC_T_HI + pb * FRAG + lane * 16) = hi;
-        *reinterpret_cast<u32x4_t *>(rec + REC_T_LO + pb * FRAG + lane * 16) = lo;
+        *reinterpret_cast<u32x4_t *>(rec + REC_TW_HI + pb * FRAG + lane * 16) = hi;
+        *reinterpret_cast<u32x4_t *>(rec + REC_TW_LO + pb * FRAG + lane * 16) = lo;
     }
+    lds_barrier();  // P in place
+
+    // P T, 16x16 tile (tb, tj) for tj <= tb, as (P T)^T = T^T P^T on fp32
+    // MFMA: over the 16-wide blocks sa = tj .. tb of the inner index, four
+    // steps st with inner index 16 sa + 4 g + st in lane group g.  The result
+    // lane (g, r) holds PT[16 tb + r][16 tj + 4 g + e], half of the record's
+    // fragment of block (tb, tj / 2).  Tiles (each costs tb - tj + 1 blocks)
+    // are spread so that every wave does five blocks: wave 0 (3,0) (3,3);
+    // wave 1 (3,1) (3,2); wave 2 (2,0) (2,1); wave 3 (1,0) (1,1) (2,2) (0,0).
+    // The tiles above the diagonal inside fragments, (0,1) and (2,3), are
+    // written as zeros with (0,0) and (2,2).
+    {
+        const uint32_t tiles = wave == 0 ? 0x3330u : wave == 1 ? 0x3231u : wave == 2 ? 0x2120u : 0x00221110u;
+        const int count = wave == 3 ? 4 : 2;
+        for (int x = 0; x < count; ++x) {
+            const int code = (tiles >> (8 * x)) & 0xFF, tb = code >> 4, tj = code & 15;
+            f32x4_t acc = zero4();
+            for (int sa = tj; sa <= tb; ++sa)
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const int kx = 16 * sa + 4 * g4 + st;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(*tref(S.QT, kx, 16 * tj + r), *tref(S.KL, 16 * tb + r, kx),
+                                                               acc, 0, 0, 0);
+                }
+            u32x2_t hi, lo;
+            split4(acc, hi, lo);
+            const int pb = tblk(tb, tj >> 1);
+            char *fh = rec + REC_PT_HI + pb * FRAG + lane * 16, *fl = rec + REC_PT_LO + pb * FRAG + lane * 16;
+            if ((tj & 1) == 0 && tj + 1 > tb) {  // the fragment's other half is above the diagonal
+                *reinterpret_cast<u32x4_t *>(fh) = u32x4_t{hi[0], hi[1], 0u, 0u};
+                *reinterpret_cast<u32x4_t *>(fl) = u32x4_t{lo[0], lo[1], 0u, 0u};
+            } else {
+                *reinterpret_cast<u32x2_t *>(fh + (tj & 1) * 8) = hi;
+                *reinterpret_cast<u32x2_t *>(fl + (tj & 1) * 8) = lo;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Precision of the chains' products that take an fp32 operand.  Each fp32
+// operand is split into bf16 hi + lo (gdn_mfma.h); a product keeps
+//   SPLIT_BOTH  hi*hi + hi*lo + lo*hi (both operands fp32)
+//   SPLIT_A     A hi + lo, B exact or hi only
+//   SPLIT_B     B hi + lo, A exact or hi only
+//   HI_ONLY     hi*hi
+enum Prec { HI_ONLY = 1, SPLIT_A = 2, SPLIT_B = 3, SPLIT_BOTH = 4 };
+constexpr Prec PREC_KS = SPLIT_B;      // K S0^T and Q S0^T (K, Q exact bf16; S0 fp32)
+constexpr Prec PREC_TWY = SPLIT_BOTH;  // Tw Y (both fp32)
+constexpr Prec PREC_PTY = SPLIT_BOTH;  // (P T) Y (both fp32)
+constexpr Prec PREC_UPD = SPLIT_B;     // K^T (Tw Y) (K exact; Tw Y fp32)
+
+template <Prec P>
+__device__ __forceinline__ f32x4_t mfma_p(u32x4_t ahi, u32x4_t alo, u32x4_t bhi, u32x4_t blo, f32x4_t d) {
+    if constexpr (P == SPLIT_BOTH) return mfma3(ahi, alo, bhi, blo, d);
+    if constexpr (P == SPLIT_A) return mfma2a(ahi, alo, bhi, d);
+    if constexpr (P == SPLIT_B) return mfma2b(ahi, bhi, blo, d);
+    return mfma(ahi, bhi, d);
 }
 
 // ---------------------------------------------------------------------------
@@ -641,15 +725,17 @@ __device__ __forceinline__ void chain_copies(ChainBuf &B, const char *rec, const
     }
 }
 
-// NW compute waves (16 rows of S each) and NW copy waves per workgroup.  The
-// copy waves move chunk c + 1 into LDS while the compute waves work on chunk
-// c; one barrier per chunk hands the buffers over.
-template <int NW>
-__global__ __launch_bounds__(128 * NW) void k_chunk_chain(
+// CHAIN_NW compute waves (16 rows of S each) and as many copy waves per
+// workgroup, two workgroups per (sequence, head).  The copy waves move chunk
+// c + 1 into LDS while the compute waves work on chunk c; one barrier per
+// chunk hands the buffers over.
+constexpr int CHAIN_NW = 4;
+__global__ __launch_bounds__(128 * CHAIN_NW) void k_chunk_chain(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ seq_order,
     int n_seq, int64_t total_tokens, int H, const float *initial_state, float *__restrict__ o, float *final_state,
     const char *__restrict__ recs) {
+    constexpr int NW = CHAIN_NW;
     constexpr int TILES = DK / (16 * NW);
     const int bid = blockIdx.x;
     // All row tiles of one (sequence, head) share bid % 8, so they run on one XCD and share its L2.
@@ -701,10 +787,10 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
         const int64_t t0 = seq_t0 + (int64_t)c * C;
         const int n = (int)min((int64_t)C, L - (int64_t)c * C);
         const ChainBuf &B = buf[c & 1];
-        const u32x4_t *Th = reinterpret_cast<const u32x4_t *>(B.rec + REC_T_HI);
-        const u32x4_t *Tl = reinterpret_cast<const u32x4_t *>(B.rec + REC_T_LO);
-        const u32x4_t *Ph = reinterpret_cast<const u32x4_t *>(B.rec + REC_P_HI);
-        const u32x4_t *Pl = reinterpret_cast<const u32x4_t *>(B.rec + REC_P_LO);
+        const u32x4_t *Twh = reinterpret_cast<const u32x4_t *>(B.rec + REC_TW_HI);
+        const u32x4_t *Twl = reinterpret_cast<const u32x4_t *>(B.rec + REC_TW_LO);
+        const u32x4_t *PTh = reinterpret_cast<const u32x4_t *>(B.rec + REC_PT_HI);
+        const u32x4_t *PTl = reinterpret_cast<const u32x4_t *>(B.rec + REC_PT_LO);
         const float *gate = reinterpret_cast<const float *>(B.rec + REC_GATE);
 
         // X = K S0^T and O = Q S0^T (one shared split operand S0^T)
@@ -718,8 +804,8 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
             O[tb] = zero4();
 #pragma unroll
             for (int kj = 0; kj < 4; ++kj) {
-                X[tb] = mfma2b(rowfrag(B.K, 16 * tb, kj, g4, r), bSh[kj], bSl[kj], X[tb]);
-                O[tb] = mfma2b(rowfrag(B.Q, 16 * tb, kj, g4, r), bSh[kj], bSl[kj], O[tb]);
+                X[tb] = mfma_p<PREC_KS>(rowfrag(B.K, 16 * tb, kj, g4, r), u32x4_t{}, bSh[kj], bSl[kj], X[tb]);
+                O[tb] = mfma_p<PREC_KS>(rowfrag(B.Q, 16 * tb, kj, g4, r), u32x4_t{}, bSh[kj], bSl[kj], O[tb]);
             }
         }
         // Y = V - diag(e^{G_{t-1}}) X, in accumulator layout (tiles 2 ks and 2 ks + 1 from one V^T fragment)
@@ -739,25 +825,18 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
             }
             split_pair(y[0], y[1], bYh[ks], bYl[ks]);
         }
-        // U = T Y
-        f32x4_t U[4];
+        // W = Tw Y (the update's pseudo-values) and O = diag(e^{G_t}) Q S0^T + (P T) Y
+        f32x4_t W[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            U[tb] = zero4();
-#pragma unroll
-            for (int ks = 0; ks <= (tb >> 1); ++ks)
-                U[tb] = mfma3(Th[tblk(tb, ks) * 64 + lane], Tl[tblk(tb, ks) * 64 + lane], bYh[ks], bYl[ks], U[tb]);
-        }
-        // O = diag(e^{G_t}) Q S0^T + P U
-        u32x4_t bUh[2], bUl[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
+            W[tb] = zero4();
             O[tb] *= *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * tb + 4 * g4);
 #pragma unroll
-            for (int ks = 0; ks <= (tb >> 1); ++ks)
-                O[tb] = mfma3(Ph[tblk(tb, ks) * 64 + lane], Pl[tblk(tb, ks) * 64 + lane], bUh[ks], bUl[ks], O[tb]);
+            for (int ks = 0; ks <= (tb >> 1); ++ks) {
+                const int bk = tblk(tb, ks);
+                W[tb] = mfma_p<PREC_TWY>(Twh[bk * 64 + lane], Twl[bk * 64 + lane], bYh[ks], bYl[ks], W[tb]);
+                O[tb] = mfma_p<PREC_PTY>(PTh[bk * 64 + lane], PTl[bk * 64 + lane], bYh[ks], bYl[ks], O[tb]);
+            }
         }
         float *ob = o + t0 * rs + h * DK;  // o is stored non-temporally (measured about 3% faster)
         const int ooff = 4 * g4 * rs + iw + r;
@@ -774,18 +853,17 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
                     if (16 * tb + 4 * g4 + e < n) __builtin_nontemporal_store(O[tb][e], &ob[ooff + (16 * tb + e) * rs]);
         }
 
-        // S0^T <- e^{G_n} S0^T + K^T diag(beta_t e^{G_n - G_t}) U
+        // S0^T <- e^{G_n} S0^T + K^T W
+        u32x4_t bWh[2], bWl[2];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) U[tb] *= *reinterpret_cast<const f32x4_t *>(gate + GATE_BW + 16 * tb + 4 * g4);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
+        for (int ks = 0; ks < 2; ++ks) split_pair(W[2 * ks], W[2 * ks + 1], bWh[ks], bWl[ks]);
         const float eGn = gate[GATE_EGN];
 #pragma unroll
         for (int jm = 0; jm < 8; ++jm) {
             St[jm] *= eGn;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                St[jm] = mfma2b(colfrag_st(B.K, ks, jm, g4, lane), bUh[ks], bUl[ks], St[jm]);
+                St[jm] = mfma_p<PREC_UPD>(colfrag_st(B.K, ks, jm, g4, lane), u32x4_t{}, bWh[ks], bWl[ks], St[jm]);
         }
         lds_barrier();  // chunk c + 1 is in the other buffer, and this one is free
     }
@@ -800,11 +878,14 @@ __global__ __launch_bounds__(128 * NW) void k_chunk_chain(
 //
 // Four workgroups per (sequence, head), each owning 32 rows of S (two 16-row
 // slices).  Each slice's 128 columns are split over two compute waves of 64
-// columns: a wave forms the partial products K S0^T and Q S0^T over its
-// columns, the pair swaps partials through LDS, and both then hold the full
-// X and Q S0^T of their slice.  Both solve U = T Y (the same 18 MFMAs), each
-// writes two of the four 16-token output tiles, and each updates its own 64
-// columns of S.  Four copy waves stream the next chunk: the record, q and k
+// columns: a wave forms the partial product K S0^T over its columns and the
+// pair swaps partials through LDS, so that both hold the full X of their
+// slice.  Both then form Y and W = Tw Y (the same 18 MFMAs), and each updates
+// its own 64 columns of S.  The outputs are not on that path: each wave also
+// forms its columns' partial Q S0^T (scaled by e^{G_t}) and (P T) Y for two of
+// the four 16-token output tiles, hands the partner the partial Q S0^T of the
+// partner's two tiles through LDS, and completes and stores its tiles during
+// the next chunk (after the last chunk, once the loop ends).  Four copy waves stream the next chunk: the record, q and k
 // row tiles, and the workgroup's 32 columns of v (64-byte rows).
 
 constexpr int CS_TILES = 4;             // workgroups per (sequence, head)
@@ -816,31 +897,41 @@ struct ChainBufCS {
     char K[TILE];
     char V[VC_BYTES];
 };
+// Exchange slots per compute wave, by lane: tiles 0..3 the partial X; in
+// CS_OUT tiles 4, 5 (even chunks) or 6, 7 (odd chunks) the partial
+// e^{G_t} Q S0^T of the partner's two output tiles (written in one chunk,
+// read in the next), in CS_PAIR tiles 4..7 the partial X of the second state.
 struct ChainSmemCS {
     ChainBufCS buf[2];
-    f32x4_t xch[4][8][64];  // per compute wave: partial X (tiles 0..3) and Q S0^T (tiles 4..7), by lane
+    f32x4_t xch[4][8][64];
     char scratch[FRAG];     // target of the copy waves' padding loads and line touches
 };
 
-// Compact v tile: row t holds 32 columns (64 bytes) at t * 64.  Piece a
-// (one kilobyte) is rows 16a .. 16a + 15; lane l copies row 16a + (l >> 2),
-// columns 8 (l & 3) .. + 7 of the workgroup's 32.
+// Compact v tile: row t holds 32 columns (64 bytes) at t * 64, its two
+// 32-byte halves swapped when bit 2 of t is set, so that the transposing
+// reads below (8 tokens t, t + 4 in one pass) touch every LDS bank once.
+// Piece a (one kilobyte) is rows 16a .. 16a + 15; lane l fills 16-byte unit
+// (l & 3) of row 16a + (l >> 2) with the matching 8 of the workgroup's 32
+// columns.
+__device__ __forceinline__ int vc_half(int t) { return (t >> 2) & 1; }
 __device__ __forceinline__ void dma_vcols(char *tile, const uint16_t *chunk, int rs, int n, int lane, int a) {
     const int t = 16 * a + (lane >> 2);
-    const uint16_t *src = chunk + (uint32_t)(min(t, n - 1) * rs + 8 * (lane & 3));
+    const int unit = (lane & 3) ^ (2 * vc_half(t));
+    const uint16_t *src = chunk + (uint32_t)(min(t, n - 1) * rs + 8 * unit);
     __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)(tile + a * FRAG), 16, 0, 0);
 }
 
-// Fragment of v columns col0 .. col0 + 15 of the compact tile in accumulator
-// order: lane (g, r) gets v[32 ks + slot_k(g, e)][col0 + r], e = 0..7.
-__device__ __forceinline__ u32x4_t vfrag(const char *tile, int ks, int col0, int g4, int lane) {
+// Fragment of v columns 16 sl .. 16 sl + 15 of the compact tile in
+// accumulator order: lane (g, r) gets v[32 ks + slot_k(g, e)][16 sl + r], e = 0..7.
+__device__ __forceinline__ u32x4_t vfrag(const char *tile, int ks, int sl, int g4, int lane) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     const int L = lane & 15, e = L >> 2, m = L & 3;
-    const int t0 = 32 * ks + 4 * g4 + e, t1 = t0 + 16;
+    const int t0 = 32 * ks + 4 * g4 + e, t1 = t0 + 16;  // vc_half(t1) == vc_half(t0)
+    const int off = 32 * (sl ^ vc_half(t0)) + m * 8;
     const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(tile + t0 * 64 + col0 * 2 + m * 8));
+        (__attribute__((address_space(3))) v4i16 *)(tile + t0 * 64 + off));
     const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(tile + t1 * 64 + col0 * 2 + m * 8));
+        (__attribute__((address_space(3))) v4i16 *)(tile + t1 * 64 + off));
     const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
     return u32x4_t{a2[0], a2[1], b2[0], b2[1]};
 }
@@ -886,10 +977,7 @@ __device__ __forceinline__ void cs_copies(ChainBufCS &B, char *scratch, const ch
 // The 128-byte lines of one chunk's copies: the record, then two lines per
 // q, k and v row (rows past n clamped to n - 1).
 constexpr int PF_LINES = REC_BYTES / 128 + 3 * 2 * C;
-#ifndef GDN_PF_DIST
-#define GDN_PF_DIST 3
-#endif
-constexpr int PF_DIST = GDN_PF_DIST;  // chunks between the touch of a chunk's lines and its copies
+constexpr int PF_DIST = 3;  // chunks between the touch of a chunk's lines and its copies
 
 __device__ __forceinline__ const uint32_t *chunk_line(const char *rec, const uint16_t *q, const uint16_t *k,
                                                       const uint16_t *v, int64_t rowbase, int rs, int n, int line) {
@@ -943,8 +1031,8 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         // Touch chunk c: the first 16 bytes of each 128-byte line in this
         // workgroup's quarter of the lines (the four workgroups of a pair share
         // them out), copied to a scratch kilobyte of LDS.  The copies of that
-        // chunk, two chunks later, then hit in L2.  Lanes past the quarter
-        // re-touch line 0, so every wave issues exactly one load.
+        // chunk, PF_DIST - 1 chunks later, then hit in L2.  Lanes past the
+        // quarter re-touch line 0, so every wave issues exactly one load.
         auto touch = [=](int c) {
             int line = tile + CS_TILES * (cw * 64 + lane);
             if (line >= PF_LINES) line = 0;
@@ -990,6 +1078,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     }
 
     const int sl = wave >> 1, hf = wave & 1;  // row slice, column half
+    const int partner = wave ^ 1;
     const int iw = tile * 32 + 16 * sl;       // first row of S owned by this wave
     // S^T in accumulators, this wave's 64 columns: St[j] lane (g4, r) holds S[iw + r][64 hf + st_col(j, g4) + e]
     f32x4_t St[4], Sm[4];  // Sm: the pair's second state (CS_PAIR only)
@@ -1002,75 +1091,116 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         St[j] = initial_state ? *reinterpret_cast<const f32x4_t *>(initial_state + sbase + st_col(j, g4)) : zero4();
         Sm[j] = pair ? eye : zero4();
     }
-    // output tiles of this wave: {0, 3} or {1, 2} (balanced P U work)
+    // split S0^T (this wave's 64 columns: k steps 2 hf, 2 hf + 1), kept across the chunk boundary
+    u32x4_t bSh[2], bSl[2], bMh[2], bMl[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        split_pair(St[2 * kk], St[2 * kk + 1], bSh[kk], bSl[kk]);
+        if (pair) split_pair(Sm[2 * kk], Sm[2 * kk + 1], bMh[kk], bMl[kk]);
+    }
+    // output tiles of this wave: {0, 3} or {1, 2} (balanced (P T) Y work); the partner's are the other two
     const int ta = hf ? 1 : 0, tz = hf ? 2 : 3;
+    const int pa = hf ? 0 : 1, pz = hf ? 3 : 2;
+    const int ooff = 4 * g4 * rs + iw + r;
+    // the previous chunk's own output tiles, waiting for the partner's partial Q S0^T
+    f32x4_t Oa = zero4(), Oz = zero4();
+    auto store_outputs = [&](int cprev) {
+        const int64_t t0 = seq_t0 + (int64_t)cprev * C;
+        const int n = (int)min((int64_t)C, L - (int64_t)cprev * C);
+        float *ob = o + t0 * rs + h * DK;  // o is stored non-temporally (measured about 3% faster)
+        const int slot = 4 + 2 * (cprev & 1);
+        const f32x4_t fa = Oa + sm.xch[partner][slot][lane], fz = Oz + sm.xch[partner][slot + 1][lane];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int tb = x ? tz : ta;
+            const f32x4_t val = x ? fz : fa;
+            if (n == C) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) __builtin_nontemporal_store(val[e], &ob[ooff + (16 * tb + e) * rs]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (16 * tb + 4 * g4 + e < n) __builtin_nontemporal_store(val[e], &ob[ooff + (16 * tb + e) * rs]);
+            }
+        }
+    };
 
     lds_barrier();  // A_0: chunk 0 is in buf[0]
     for (int c = 0; c < nc; ++c) {
-        const int64_t t0 = seq_t0 + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, L - (int64_t)c * C);
         const ChainBufCS &B = sm.buf[c & 1];
-        const u32x4_t *Th = reinterpret_cast<const u32x4_t *>(B.rec + REC_T_HI);
-        const u32x4_t *Tl = reinterpret_cast<const u32x4_t *>(B.rec + REC_T_LO);
-        const u32x4_t *Ph = reinterpret_cast<const u32x4_t *>(B.rec + REC_P_HI);
-        const u32x4_t *Pl = reinterpret_cast<const u32x4_t *>(B.rec + REC_P_LO);
+        const u32x4_t *Twh = reinterpret_cast<const u32x4_t *>(B.rec + REC_TW_HI);
+        const u32x4_t *Twl = reinterpret_cast<const u32x4_t *>(B.rec + REC_TW_LO);
+        const u32x4_t *PTh = reinterpret_cast<const u32x4_t *>(B.rec + REC_PT_HI);
+        const u32x4_t *PTl = reinterpret_cast<const u32x4_t *>(B.rec + REC_PT_LO);
         const float *gate = reinterpret_cast<const float *>(B.rec + REC_GATE);
 
-        // T and this wave's P blocks, read first: their LDS latency then hides
-        // behind the partial products (the buffer is stable until A_{c+1})
-        u32x4_t tfh[T_BLOCKS], tfl[T_BLOCKS];
-#pragma unroll
-        for (int b = 0; b < T_BLOCKS; ++b) {
-            tfh[b] = Th[b * 64 + lane];
-            tfl[b] = Tl[b * 64 + lane];
-        }
-        const int pz = tblk(tz, 0);  // tile tz in {2, 3} has blocks pz, pz + 1; tile ta in {0, 1} is block ta
-        u32x4_t pah, pal, pz0h, pz0l, pz1h, pz1l;
-        if (outs) {
-            pah = Ph[ta * 64 + lane];
-            pal = Pl[ta * 64 + lane];
-            pz0h = Ph[pz * 64 + lane];
-            pz0l = Pl[pz * 64 + lane];
-            pz1h = Ph[(pz + 1) * 64 + lane];
-            pz1l = Pl[(pz + 1) * 64 + lane];
-        }
-
-        // partial X = K S0^T and Q S0^T over this wave's 64 columns (k steps 2 hf, 2 hf + 1)
-        u32x4_t bSh[2], bSl[2], bMh[2], bMl[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            split_pair(St[2 * kk], St[2 * kk + 1], bSh[kk], bSl[kk]);
-            if (pair) split_pair(Sm[2 * kk], Sm[2 * kk + 1], bMh[kk], bMl[kk]);
-        }
-        // O: Q S0^T (CS_OUT), or the pair's K Sm^T (CS_PAIR), exchanged in the same slots
-        f32x4_t X[4], O[4];
+        // partial X = K S0^T over this wave's 64 columns (and the pair's K Sm^T)
+        f32x4_t X[4], Xm[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             X[tb] = zero4();
-            O[tb] = zero4();
+            Xm[tb] = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const u32x4_t kf = rowfrag(B.K, 16 * tb, 2 * hf + kk, g4, r);
-                X[tb] = mfma2b(kf, bSh[kk], bSl[kk], X[tb]);
-                if (outs) O[tb] = mfma2b(rowfrag(B.Q, 16 * tb, 2 * hf + kk, g4, r), bSh[kk], bSl[kk], O[tb]);
-                if (pair) O[tb] = mfma2b(kf, bMh[kk], bMl[kk], O[tb]);
+                X[tb] = mfma_p<PREC_KS>(kf, u32x4_t{}, bSh[kk], bSl[kk], X[tb]);
+                if (pair) Xm[tb] = mfma_p<PREC_KS>(kf, u32x4_t{}, bMh[kk], bMl[kk], Xm[tb]);
             }
             sm.xch[wave][tb][lane] = X[tb];
-            sm.xch[wave][4 + tb][lane] = O[tb];
+            if (pair) sm.xch[wave][4 + tb][lane] = Xm[tb];
         }
         lds_barrier();  // X_c: partials visible
+
+        // Tw and this wave's (P T) blocks: the buffer is stable until A_{c+1}
+        u32x4_t tfh[T_BLOCKS], tfl[T_BLOCKS];
+#pragma unroll
+        for (int bk = 0; bk < T_BLOCKS; ++bk) {
+            tfh[bk] = Twh[bk * 64 + lane];
+            tfl[bk] = Twl[bk * 64 + lane];
+        }
+        const int bz = tblk(tz, 0);  // tile tz in {2, 3} has blocks bz, bz + 1; tile ta in {0, 1} is block ta
+        u32x4_t pah, pal, pz0h, pz0l, pz1h, pz1l;
+        if (outs) {
+            pah = PTh[ta * 64 + lane];
+            pal = PTl[ta * 64 + lane];
+            pz0h = PTh[bz * 64 + lane];
+            pz0l = PTl[bz * 64 + lane];
+            pz1h = PTh[(bz + 1) * 64 + lane];
+            pz1l = PTl[(bz + 1) * 64 + lane];
+        }
+        // K^T fragments of the state update, read now (k is stable until A_{c+1})
+        u32x4_t kst[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) kst[j][ks] = colfrag_st(B.K, ks, 4 * hf + j, g4, lane);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            X[tb] += sm.xch[wave ^ 1][tb][lane];
-            if (pair || tb == ta || tb == tz) O[tb] += sm.xch[wave ^ 1][4 + tb][lane];  // static indices, uniform test
+            X[tb] += sm.xch[partner][tb][lane];
+            if (pair) Xm[tb] += sm.xch[partner][4 + tb][lane];
+        }
+        // partial e^{G_t} Q S0^T over this wave's columns for the four tiles,
+        // in the order ta, tz (own, kept) and pa, pz (the partner's, to its slots)
+        f32x4_t QS[4];
+        if (outs) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int tb = x == 0 ? ta : x == 1 ? tz : x == 2 ? pa : pz;  // wave-uniform
+                QS[x] = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    QS[x] = mfma_p<PREC_KS>(rowfrag(B.Q, 16 * tb, 2 * hf + kk, g4, r), u32x4_t{}, bSh[kk], bSl[kk],
+                                            QS[x]);
+                QS[x] *= *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * tb + 4 * g4);
+            }
         }
 
-        // Y = V - diag(e^{G_{t-1}}) X
-        u32x4_t bYh[2], bYl[2];
+        // Y = V - diag(e^{G_{t-1}}) X (and the pair's Ym = -diag(e^{G_{t-1}}) Xm)
+        u32x4_t bYh[2], bYl[2], bYmh[2], bYml[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const u32x4_t vf = vfrag(B.V, ks, 16 * sl, g4, lane);
-            f32x4_t y[2];
+            const u32x4_t vf = vfrag(B.V, ks, sl, g4, lane);
+            f32x4_t y[2], ym[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int tb = 2 * ks + hh;
@@ -1079,75 +1209,42 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
                 const f32x4_t vv = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u),
                                     __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xFFFF0000u)};
                 y[hh] = vv - em * X[tb];
+                if (pair) ym[hh] = -(em * Xm[tb]);
             }
             split_pair(y[0], y[1], bYh[ks], bYl[ks]);
+            if (pair) split_pair(ym[0], ym[1], bYmh[ks], bYml[ks]);
         }
-        // U = T Y (and the pair's Um = T Ym, Ym = -diag(e^{G_{t-1}}) Xm)
-        u32x4_t bYmh[2], bYml[2];
-        if (pair) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                f32x4_t y[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int tb = 2 * ks + hh;
-                    const f32x4_t em = *reinterpret_cast<const f32x4_t *>(gate + GATE_EGM1 + 16 * tb + 4 * g4);
-                    y[hh] = -(em * O[tb]);
-                }
-                split_pair(y[0], y[1], bYmh[ks], bYml[ks]);
-            }
-        }
-        f32x4_t U[4], Um[4];
+        // W = Tw Y (and Wm = Tw Ym)
+        f32x4_t W[4], Wm[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            U[tb] = zero4();
-            Um[tb] = zero4();
+            W[tb] = zero4();
+            Wm[tb] = zero4();
 #pragma unroll
             for (int ks = 0; ks <= (tb >> 1); ++ks) {
-                U[tb] = mfma3(tfh[tblk(tb, ks)], tfl[tblk(tb, ks)], bYh[ks], bYl[ks], U[tb]);
-                if (pair) Um[tb] = mfma3(tfh[tblk(tb, ks)], tfl[tblk(tb, ks)], bYmh[ks], bYml[ks], Um[tb]);
+                W[tb] = mfma_p<PREC_TWY>(tfh[tblk(tb, ks)], tfl[tblk(tb, ks)], bYh[ks], bYl[ks], W[tb]);
+                if (pair) Wm[tb] = mfma_p<PREC_TWY>(tfh[tblk(tb, ks)], tfl[tblk(tb, ks)], bYmh[ks], bYml[ks], Wm[tb]);
             }
         }
-        // O = diag(e^{G_t}) Q S0^T + P U for this wave's two tiles
-        u32x4_t bUh[2], bUl[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
-        float *ob = o + t0 * rs + h * DK;  // o is stored non-temporally (measured about 3% faster)
-        const int ooff = 4 * g4 * rs + iw + r;
+        // the previous chunk's outputs (the partner's partials of it are in
+        // the other parity's slots), then this chunk's own output tiles:
+        // e^{G_t} Q S0^T (own columns) + (P T) Y
         if (outs) {
-            const f32x4_t Oa = hf ? O[1] : O[0], Oz = hf ? O[2] : O[3];  // tiles ta, tz (uniform selects)
-            f32x4_t acc[2];
-            acc[0] = Oa * *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * ta + 4 * g4);
-            acc[0] = mfma3(pah, pal, bUh[0], bUl[0], acc[0]);
-            acc[1] = Oz * *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * tz + 4 * g4);
-            acc[1] = mfma3(pz0h, pz0l, bUh[0], bUl[0], acc[1]);
-            acc[1] = mfma3(pz1h, pz1l, bUh[1], bUl[1], acc[1]);
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int tb = x ? tz : ta;
-                if (n == C) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) __builtin_nontemporal_store(acc[x][e], &ob[ooff + (16 * tb + e) * rs]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (16 * tb + 4 * g4 + e < n) __builtin_nontemporal_store(acc[x][e], &ob[ooff + (16 * tb + e) * rs]);
-                }
-            }
+            if (c > 0) store_outputs(c - 1);
+            const int slot = 4 + 2 * (c & 1);
+            sm.xch[wave][slot][lane] = QS[2];  // the partner's tiles pa, pz
+            sm.xch[wave][slot + 1][lane] = QS[3];
+            Oa = mfma_p<PREC_PTY>(pah, pal, bYh[0], bYl[0], QS[0]);
+            Oz = mfma_p<PREC_PTY>(pz0h, pz0l, bYh[0], bYl[0], QS[1]);
+            Oz = mfma_p<PREC_PTY>(pz1h, pz1l, bYh[1], bYl[1], Oz);
         }
 
-        // S0^T <- e^{G_n} S0^T + K^T diag(beta_t e^{G_n - G_t}) U, this wave's 64 columns
-        u32x4_t bUmh[2], bUml[2];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            const f32x4_t bw = *reinterpret_cast<const f32x4_t *>(gate + GATE_BW + 16 * tb + 4 * g4);
-            U[tb] *= bw;
-            if (pair) Um[tb] *= bw;
-        }
+        // S0^T <- e^{G_n} S0^T + K^T W, this wave's 64 columns
+        u32x4_t bWh[2], bWl[2], bWmh[2], bWml[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            split_pair(U[2 * ks], U[2 * ks + 1], bUh[ks], bUl[ks]);
-            if (pair) split_pair(Um[2 * ks], Um[2 * ks + 1], bUmh[ks], bUml[ks]);
+            split_pair(W[2 * ks], W[2 * ks + 1], bWh[ks], bWl[ks]);
+            if (pair) split_pair(Wm[2 * ks], Wm[2 * ks + 1], bWmh[ks], bWml[ks]);
         }
         const float eGn = gate[GATE_EGN];
 #pragma unroll
@@ -1156,13 +1253,18 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             if (pair) Sm[j] *= eGn;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const u32x4_t kf = colfrag_st(B.K, ks, 4 * hf + j, g4, lane);
-                St[j] = mfma2b(kf, bUh[ks], bUl[ks], St[j]);
-                if (pair) Sm[j] = mfma2b(kf, bUmh[ks], bUml[ks], Sm[j]);
+                St[j] = mfma_p<PREC_UPD>(kst[j][ks], u32x4_t{}, bWh[ks], bWl[ks], St[j]);
+                if (pair) Sm[j] = mfma_p<PREC_UPD>(kst[j][ks], u32x4_t{}, bWmh[ks], bWml[ks], Sm[j]);
             }
         }
-        lds_barrier();  // A_{c+1}: chunk c + 1 is in the other buffer, and this one is free
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            split_pair(St[2 * kk], St[2 * kk + 1], bSh[kk], bSl[kk]);
+            if (pair) split_pair(Sm[2 * kk], Sm[2 * kk + 1], bMh[kk], bMl[kk]);
+        }
+        lds_barrier();  // A_{c+1}: chunk c + 1 is in the other buffer, this one is free, the partials are visible
     }
+    if (outs && nc > 0) store_outputs(nc - 1);
 
     float *dst = final_state + sbase;
 #pragma unroll
@@ -1191,15 +1293,15 @@ hipError_t launch_chain_cs(const void *q, const void *k, const void *v, const in
     return hipGetLastError();
 }
 
-template <int NW>
 hipError_t launch_chain(const void *q, const void *k, const void *v, const int32_t *cu, const int32_t *chunk_base,
                         const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H,
                         const float *initial_state, float *o, float *final_state, const char *recs,
                         hipStream_t stream) {
+    constexpr int NW = CHAIN_NW;
     constexpr int TILES = DK / (16 * NW);
     const int64_t units = n_seq * H;
     const int64_t grid = ((units + 7) / 8) * 8 * TILES;
-    hipLaunchKernelGGL((k_chunk_chain<NW>), dim3((unsigned)grid), dim3(128 * NW), 0, stream,
+    hipLaunchKernelGGL(k_chunk_chain, dim3((unsigned)grid), dim3(128 * NW), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), cu, chunk_base, seq_order,
                        (int)n_seq, total_tokens, H, initial_state, o, final_state, recs);
@@ -1322,20 +1424,6 @@ __global__ __launch_bounds__(512) void k_scan_combine(int n_seq, int H, const in
     }
 }
 
-// Compute waves per chain workgroup (it has as many copy waves).  Each compute
-// wave owns 16 rows of S; fewer per workgroup means more workgroups (more
-// CUs) per (sequence, head), each copying the whole chunk.
-// GDN_CHAIN_WAVES=2|4 overrides the choice (a tuning knob, read once).
-int chain_waves(int64_t units) {
-    static const int forced = [] {
-        const char *e = getenv("GDN_CHAIN_WAVES");
-        return e ? atoi(e) : 0;
-    }();
-    if (forced == 2 || forced == 4) return forced;
-    (void)units;
-    return 4;  // measured faster than 2 even when 2 would fill more CUs (fewer record copies per head)
-}
-
 // The column-split chain (four workgroups per pair, a shorter step per chunk)
 // when it runs every pair in little more than the longest pair's time: the
 // workgroups of the long sequences (more than half the longest's chunks) all
@@ -1344,13 +1432,8 @@ int chain_waves(int64_t units) {
 // it is throughput-bound, and the two-workgroup form, with half the workgroups
 // and copies per pair, is faster (measured on packed batches of 8 sequences
 // of 1,224 to 54,318 tokens: 24 heads favour the column split, 48 heads the
-// two-workgroup form).  GDN_CHAIN_SPLIT=0|1 overrides (a tuning knob, read once).
+// two-workgroup form).
 bool use_column_split(int64_t sum_chunks, int64_t max_chunks, int64_t n_long, int H) {
-    static const int forced = [] {
-        const char *e = getenv("GDN_CHAIN_SPLIT");
-        return e ? atoi(e) : -1;
-    }();
-    if (forced == 0 || forced == 1) return forced == 1;
     return CS_TILES * (int64_t)H * n_long <= 256 && 10 * CS_TILES * (int64_t)H * sum_chunks <= 11 * 256 * max_chunks;
 }
 
@@ -1448,12 +1531,9 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     } else if (use_column_split(n_chunks, max_chunks, n_long, H))
         e = launch_chain_cs(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
                             final_state, recs, stream);
-    else if (chain_waves(n_seq * H) == 4)
-        e = launch_chain<4>(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
-                            final_state, recs, stream);
     else
-        e = launch_chain<2>(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
-                            final_state, recs, stream);
+        e = launch_chain(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
+                         final_state, recs, stream);
     if (e != hipSuccess) return e;
     return record_mark(marks[2], stream);
 }

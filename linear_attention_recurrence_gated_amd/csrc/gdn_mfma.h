@@ -46,11 +46,24 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-// (a, b) -> hi = bf16(a), bf16(b) and lo = bf16(a - hi_a), bf16(b - hi_b), one dword each
+// (a, b) -> hi = bf16(a), bf16(b) and lo = bf16(a - hi_a), bf16(b - hi_b), one dword each.
+// a - hi_a is exact in fp32 (hi_a is a rounded to 8 significant bits); it is
+// formed as the bf16 dot product (hi_a, hi_b) . (-1, 0) + a, one instruction
+// instead of an unpack and a subtraction (likewise (0, -1) for b).  Only a
+// value below the smallest normal float could lose its hi part there (a
+// flushed bf16 operand), an absolute error under 1.2e-38.  The two constant
+// operands are kept opaque (scalar registers): the compiler would otherwise
+// encode the pair (-1, 0) as the inline constant -1.0, which the hardware
+// does not read as that pair for a packed bf16 operand.
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    uint32_t m_lo = 0x0000BF80u, m_hi = 0xBF800000u;  // (-1, 0) and (0, -1)
+    asm("" : "+s"(m_lo), "+s"(m_hi));
     hi = cvt_pk_bf16(a, b);
-    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xFFFF0000u);
-    lo = cvt_pk_bf16(a - ha, b - hb);
+    const bf16x2_t h = __builtin_bit_cast(bf16x2_t, hi);
+    const float la = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2_t, m_lo), a, false);
+    const float lb = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2_t, m_hi), b, false);
+    lo = cvt_pk_bf16(la, lb);
 }
 
 // x[0..7] -> (hi, lo) bf16 fragments

@@ -287,12 +287,9 @@ __global__ __launch_bounds__(256) void k_conv_state(const TIn *__restrict__ xq, 
         conv_state_one(xq, xk, xv, st_in, st_out, cu, total_tokens, H, D, per_seq, idx);
 }
 
-#ifndef GDN_PRE_RANGE_BF16
-#define GDN_PRE_RANGE_BF16 16
-#endif
 // Tokens per range of the long-sequence form: 16 rows of bf16 or 8 of fp32,
 // 64 VGPRs in flight either way.
-constexpr int range_long(bool bf16) { return bf16 ? GDN_PRE_RANGE_BF16 : 8; }
+constexpr int range_long(bool bf16) { return bf16 ? 16 : 8; }
 // Ranges of range_long tokens pay off when sequences are longer than a range;
 // batches of shorter ones (decode steps) take one token per range.
 int pre_range(bool bf16, int64_t n_seq, int64_t N) {
