@@ -158,6 +158,28 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
                        int32_t chunk, void *workspace, size_t workspace_bytes, int32_t variant,
                        void *stream);
 
+/* Allocation-free form of gdn_prefill, for callers that cannot allocate
+ * device memory or pass a workspace: code recorded under HIP graph capture,
+ * tight serving loops, and harnesses that forbid allocation.  Arguments,
+ * semantics and errors are those of gdn_prefill without the workspace: the
+ * kernels use a fixed scratch array of GDN_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device it runs on until the process ends (the array
+ * of the device current at the call; the stream must belong to that device).
+ * Sizes whose gdn_prefill_workspace_bytes() exceeds that limit return
+ * GDN_ERR_WORKSPACE and enqueue nothing (128 MiB covers, for example, one
+ * sequence of up to 6,912 tokens at H = 48 with d = 128).
+ * Nothing is allocated, freed or synchronised.  Every call on one device
+ * shares that device's array and leaves its contents behind (nothing in it
+ * needs to start at zero): calls that can overlap on one device, on any
+ * streams, race and must be serialised by the caller. */
+#define GDN_NOALLOC_SCRATCH_BYTES (128u << 20)
+gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v, gdn_dtype dtype,
+                               const float *g, const float *beta,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
+                               int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                               const float *initial_state, float *o, float *final_state,
+                               int32_t chunk, int32_t variant, void *stream);
+
 /* One token for each of B sequences, updating their states in place.
  *
  *   q, k    [B][H][dk] dtype;   v [B][H][dv] dtype;   g, beta [B][H] fp32

@@ -4,10 +4,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
-#include <vector>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "gdn.h"
 #include "gdn_launch.h"
@@ -89,6 +90,35 @@ int32_t pick_algorithm(gdn_dtype dtype, int32_t dk, int32_t dv, int32_t chunk) {
         case GDN_CHUNK_64_SCAN: return chunked_built ? GDN_CHUNK_64_SCAN : 0;
         default: return 0;
     }
+}
+
+// The allocation-free prefill's workspace: one fixed array per device (the
+// module's device globals are placed on every device the library runs on and
+// live until the process ends).  Host code never uses the array's name as an
+// address: the device address is looked up once per device (with that device
+// current) and kept in scratch_addr.
+static __device__ __attribute__((aligned(256))) char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch array (looked up on first use).
+hipError_t scratch_addr(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
 }
 
 // Multiplication with an overflow check against SIZE_MAX / 2.
@@ -267,6 +297,34 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
                                                  total_tokens, H, initial_state, o, final_state,
                                                  erase_of(variant), marks.ev, st),
                       "prefill (serial) launch");
+}
+
+gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v, gdn_dtype dtype, const float *g,
+                               const float *beta, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                               int64_t n_seq, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                               const float *initial_state, float *o, float *final_state, int32_t chunk,
+                               int32_t variant, void *stream) {
+    // The workspace gdn_prefill would need (0 for invalid sizes, which
+    // gdn_prefill then reports, and for the token-serial algorithm).
+    const size_t need = gdn_prefill_workspace_bytes(total_tokens, n_seq, H, dk, dv, dtype, chunk);
+    if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES) {
+        g_marks = Marks{};
+        return fail(GDN_ERR_WORKSPACE,
+                    "prefill_noalloc: these sizes need %zu bytes of workspace; the fixed scratch array holds %zu "
+                    "(use gdn_prefill with a caller workspace, or split the batch)",
+                    need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    }
+    void *ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = scratch_addr(&ws);
+        if (e != hipSuccess) {
+            g_marks = Marks{};
+            return fail(GDN_ERR_HIP, "prefill_noalloc: scratch address: %s", hipGetErrorString(e));
+        }
+    }
+    return gdn_prefill(q, k, v, dtype, g, beta, cu_seqlens, cu_seqlens_host, n_seq, total_tokens, H, dk, dv,
+                       initial_state, o, final_state, chunk, ws, need > 0 ? (size_t)GDN_NOALLOC_SCRATCH_BYTES : 0,
+                       variant, stream);
 }
 
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtype dtype, const float *g,

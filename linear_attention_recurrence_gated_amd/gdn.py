@@ -6,6 +6,7 @@ missing or fails to load, every call raises.
 
 Names mirror include/gdn.h:
     prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=0) -> (o, final_state)
+    prefill_noalloc(...)                               (the same with the library's fixed scratch)
     decode_step(q, k, v, g, beta, state) -> o          (state updated in place)
     decode_step_slots(q, k, v, g, beta, pool, slots) -> o   (slot b of the pool per row)
     state_init(state, init=None), state_reset(state, slots=None)
@@ -44,6 +45,8 @@ SIGNATURES = {
     "gdn_decode_step": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp]),
     "gdn_decode_step_slots": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i32, _i32,
                                      _i32, _i32, _vp]),
+    "gdn_prefill_noalloc": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32,
+                                   _vp, _vp, _vp, _i32, _i32, _vp]),
     "gdn_prefill_set_marks": (_i32, [ctypes.POINTER(_vp), _i32]),
     "gdn_preprocess": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
                               _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -190,6 +193,37 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=CHUNK_A
         _dev_ptr(initial_state, "initial_state", torch.float32),
         _dev_ptr(out, "out", torch.float32), _dev_ptr(final_state, "final_state", torch.float32),
         chunk, ws_ptr, ws_len, variant, _stream(dev, stream)))
+    return out, final_state
+
+
+def prefill_noalloc(q, k, v, g, beta, cu_seqlens=None, initial_state=None, chunk=CHUNK_AUTO,
+                    cu_seqlens_device=None, out=None, final_state=None, stream=None,
+                    variant=GDN_VARIANT_GATED_DELTA):
+    """prefill() through gdn_prefill_noalloc: the library's fixed per-device
+    scratch array stands in for the workspace (no device allocation inside;
+    pass out, final_state and cu_seqlens_device to allocate nothing here
+    either).  Returns (o, final_state)."""
+    import torch
+    N, H, dk = k.shape
+    dv = v.shape[2]
+    dev = k.device
+    n_seq, cu_host, cu_dev = _cu_pair(cu_seqlens, cu_seqlens_device, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    if final_state is None:
+        final_state = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=dev)
+    code = _dtype_code(k)
+    for name, t in (("q", q), ("v", v)):
+        if t.dtype != k.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from k dtype {k.dtype}")
+    cu_host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    _check(lib().gdn_prefill_noalloc(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), code,
+        _dev_ptr(g, "g", torch.float32), _dev_ptr(beta, "beta", torch.float32),
+        _dev_ptr(cu_dev, "cu_seqlens_device", torch.int32), cu_host_ptr, n_seq, N, H, dk, dv,
+        _dev_ptr(initial_state, "initial_state", torch.float32),
+        _dev_ptr(out, "out", torch.float32), _dev_ptr(final_state, "final_state", torch.float32),
+        chunk, variant, _stream(dev, stream)))
     return out, final_state
 
 

@@ -331,3 +331,16 @@ def test_launch_size_limits():
     assert st == 2 and "exceed one launch" in msg, (st, msg)
     st, msg = _preprocess(N=16 * ((1 << 24) // 3), H=16, d=128)
     assert st != 2, (st, msg)
+
+
+def test_noalloc_refuses_sizes_beyond_its_scratch():
+    """gdn_prefill_noalloc checks the workspace its sizes need against the
+    fixed scratch array before any device call."""
+    L = gdn.lib()
+    limit = 128 << 20
+    assert L.gdn_prefill_workspace_bytes(6912, 1, 48, 128, 128, gdn.GDN_BF16, gdn.CHUNK_64) <= limit
+    assert L.gdn_prefill_workspace_bytes(6913, 1, 48, 128, 128, gdn.GDN_BF16, gdn.CHUNK_64) > limit
+    st = L.gdn_prefill_noalloc(FAKE, FAKE, FAKE, gdn.GDN_BF16, FAKE, FAKE, None, None, 1, 6913, 48, 128, 128,
+                               None, FAKE * 4096, FAKE * 8192, gdn.CHUNK_64, 0, None)
+    assert gdn.STATUS[st] == "GDN_ERR_WORKSPACE"
+    assert b"scratch" in L.gdn_last_error()
