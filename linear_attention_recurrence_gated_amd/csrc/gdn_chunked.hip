@@ -1168,12 +1168,6 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             pz1h = PTh[(bz + 1) * 64 + lane];
             pz1l = PTl[(bz + 1) * 64 + lane];
         }
-        // K^T fragments of the state update, read now (k is stable until A_{c+1})
-        u32x4_t kst[4][2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) kst[j][ks] = colfrag_st(B.K, ks, 4 * hf + j, g4, lane);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             X[tb] += sm.xch[partner][tb][lane];
@@ -1253,8 +1247,9 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             if (pair) Sm[j] *= eGn;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                St[j] = mfma_p<PREC_UPD>(kst[j][ks], u32x4_t{}, bWh[ks], bWl[ks], St[j]);
-                if (pair) Sm[j] = mfma_p<PREC_UPD>(kst[j][ks], u32x4_t{}, bWmh[ks], bWml[ks], Sm[j]);
+                const u32x4_t kf = colfrag_st(B.K, ks, 4 * hf + j, g4, lane);
+                St[j] = mfma_p<PREC_UPD>(kf, u32x4_t{}, bWh[ks], bWl[ks], St[j]);
+                if (pair) Sm[j] = mfma_p<PREC_UPD>(kf, u32x4_t{}, bWmh[ks], bWml[ks], Sm[j]);
             }
         }
 #pragma unroll
