@@ -5,11 +5,10 @@ leg may import this package.  The GPU library and its Python binding never
 import, load or call it, and it shares no code with them.
 
 ``run`` wraps the double-precision token loop in ``gdn_oracle.c``:
-per head, the d_v x d_k state follows the gated delta rule of
+per head, the d_v x d_k state follows the gated delta-rule equation of
 "Qwen3.8-27B 架构深读" (feifeigd.github.io, 2026-08-17), section 三
-(Gated DeltaNet): recall ``S k`` from the ungated previous state, gate the
-state by ``g``, add ``beta (v - recall) k^T``, and read out ``o = S q`` from
-the updated state.
+(Gated DeltaNet), S_t = g_t S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T, and
+the read-out is o_t = S_t q_t from the updated state.
 """
 import ctypes
 import os

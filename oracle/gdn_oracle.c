@@ -9,24 +9,23 @@
  *
  *   Source: "Qwen3.8-27B 架构深读: Gated DeltaNet 混合线性注意力与 262K 长上下文"
  *   (feifeigd.github.io blog, 2026-08-17), section 三 (Gated DeltaNet), the
- *   gated delta-rule equation and the single-step update sketch under it.
- *   Per head, the state S is a d_v x d_k matrix, and for each token t:
+ *   gated delta-rule equation
  *
- *       r   = S_{t-1} k_t                 recall with the current key, read
- *                                         from the state BEFORE the gate
- *       S_t = g_t S_{t-1} + beta_t (v_t - r) k_t^T
- *       o_t = S_t q_t                     read-out with the query, from the
- *                                         state AFTER token t's own write
+ *       S_t = g_t S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T.
+ *
+ *   Per head, S is a d_v x d_k matrix.  The equation is evaluated as written,
+ *   for each token t: the prediction error of the previous state,
+ *
+ *       u_t = v_t - S_{t-1} k_t,
+ *
+ *   then the new state S_t = g_t S_{t-1} + beta_t u_t k_t^T, then the read-out
+ *   o_t = S_t q_t.
  *
  *   Readings taken where the page is loose:
- *   - Orientation.  The equation writes the correction as (v - S k) k^T, so S
- *     maps keys (length d_k) to values (length d_v): S is d_v x d_k.  The
- *     sketch's comment gives the transposed shape, but its recall line and its
- *     outer product only agree with the equation in this orientation.
- *   - Order.  The sketch recalls first, then scales the state by g, then adds
- *     the outer product; the equation's delta term uses S_{t-1}.  Both say the
- *     recall reads the ungated state, so the transition applied to S from the
- *     right is g_t I - beta_t k_t k_t^T.
+ *   - Orientation.  In the equation the correction is (v - S k) k^T, so S maps
+ *     keys (length d_k) to values (length d_v): S is d_v x d_k.
+ *   - The error term reads S_{t-1}, the state before the gate is applied, so
+ *     the transition applied to S from the right is g_t I - beta_t k_t k_t^T.
  *   - Output.  The page gives no GDN read-out; the linear-attention formula in
  *     the same section reads the memory with the query.  Here o_t = S_t q_t,
  *     identity feature map, no 1/sqrt(d) scale.
@@ -89,20 +88,20 @@ static void run_unit(const gdn_oracle_job *J, int64_t unit, double *r) {
         const double gt = (J->variant & 1) ? 1.0 : J->g[t * H + h];
         const double bt = J->beta[t * H + h];
         double *ot = J->o + (t * H + h) * dv;
-        /* recall from the ungated previous state (nothing is erased without
-           the erase term) */
+        /* S_{t-1} k_t, the part of the error term read from the previous state
+           (absent without the erase term) */
         for (int64_t i = 0; i < dv; ++i) {
             double acc = 0.0;
             if (!(J->variant & 2))
                 for (int64_t j = 0; j < dk; ++j) acc += S[i * dk + j] * kt[j];
             r[i] = acc;
         }
-        /* gate the old state, then write the correction along the key */
+        /* S_t = g_t S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T */
         for (int64_t i = 0; i < dv; ++i) {
             const double c = bt * (vt[i] - r[i]);
             for (int64_t j = 0; j < dk; ++j) S[i * dk + j] = gt * S[i * dk + j] + c * kt[j];
         }
-        /* read out from the updated state */
+        /* o_t = S_t q_t */
         for (int64_t i = 0; i < dv; ++i) {
             double acc = 0.0;
             for (int64_t j = 0; j < dk; ++j) acc += S[i * dk + j] * qt[j];

@@ -12,7 +12,7 @@
  *     next to their gated state.
  *   - "Qwen3.8-27B 架构深读" (feifeigd.github.io, 2026-08-17), section 三:
  *     one gate g and one write strength beta per token, g deciding how much
- *     to forget (the step sketch leaves normalisation details out).
+ *     to forget (the page leaves normalisation details out).
  * Readings taken where the pages are silent (the same on the GPU):
  *   - The convolution is causal and depthwise (one 4-tap filter per channel)
  *     over the tokens of each sequence, applied to q, k and v.  Tap 3

@@ -11,7 +11,7 @@ Sources cited below:
   [GDN]  "Qwen3.8-27B 架构深读" (feifeigd.github.io, 2026-08-17), section 三
          (Gated DeltaNet): the linear-attention memory and read-out formulas, the
          delta rule read as an online regression step ("erase along the key, then
-         write"), the gated delta-rule equation, and the single-step sketch.
+         write"), and the gated delta-rule equation.
   [PROF] "Hybrid · kết hợp nhiều cơ chế..." (openarchlab.com), section 4
          (Profiling): running in segments with carried state must not change
          the result.
