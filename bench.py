@@ -52,15 +52,19 @@ DECODE_BYTES_PER_HEAD_TOKEN = 2 * STATE_BYTES_PER_HEAD + 3 * D * 2 + 2 * 4 + D *
 # pre-processing: raw q, k, v in (bf16) + two logits, q, k, v out (bf16) + g, beta
 PRE_BYTES_PER_TOKEN_HEAD = 2 * (3 * D * 2 + 2 * 4)                                  # 1,552
 PRE_BYTES_FIXED = 3 * H * D * 4 * 4 + 2 * 9 * H * D * 2                              # taps + conv state in/out
+# the whole layer from the raw projections: raw q, k, v (bf16) + two logits in, o (fp32) out; the
+# processed q, k, v the fused call also hands back (written once, read again by its chain) are extra
+LAYER_BYTES_PER_TOKEN_HEAD = 3 * D * 2 + 2 * 4 + D * 4                              # 1,288
+LAYER_QKV_ROUND_TRIP_PER_TOKEN_HEAD = 2 * 3 * D * 2                                 # 1,536
 
 
 # Sources each measured kernel is built from: its HBM byte counts (profiles/traffic.json)
 # stay valid while these files are unchanged.
 KERNEL_SOURCES = {
-    "k_chunk_prep": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h"),
-    "k_chunk_chain": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h"),
+    "k_chunk_prep": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h", "gdn_conv.h"),
+    "k_chunk_chain": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h", "gdn_conv.h"),
     "k_decode_step": ("gdn_rowstream.hip", "gdn_device.h"),
-    "k_preprocess": ("gdn_preprocess.hip", "gdn_device.h"),
+    "k_preprocess": ("gdn_preprocess.hip", "gdn_device.h", "gdn_conv.h"),
 }
 
 
@@ -332,6 +336,170 @@ def bench_preprocess(torch, gdn, w, steps, warmup, rotate):
     return time_block(torch, call, steps)[0], time_each(torch, call, steps)
 
 
+def bench_layer(torch, gdn, w, steps, warmup, rotate):
+    """gdn_layer_prefill over the one-layer prefill shape (T = 4096, H = 48,
+    d = 128, bf16, SiLU, with conv state and gate bias, zero initial state),
+    and the same work as two calls (gdn_preprocess, then gdn_prefill), each
+    timed as a block over `rotate` resident copies of the raw inputs.  Returns
+    (layer ms, two-call ms, per-kernel ms of the layer call from the library's
+    marks)."""
+    inp = w.make_preprocess([T], H=H, d=D, dtype="bf16", seed=w.SEED_BASE + 6, activation="silu", packed=False)
+    dev = "cuda:0"
+    f = lambda x: torch.from_numpy(x).to(dev)
+    bf = lambda x: w.to_torch(x, "bf16", dev)
+    sets = [dict(xq=bf(inp.xq), xk=bf(inp.xk), xv=bf(inp.xv), a=f(inp.a_logit), b=f(inp.b_logit),
+                 st=bf(inp.state_in), o=torch.empty((T, H, D), dtype=torch.float32, device=dev),
+                 s=torch.empty((1, H, D, D), dtype=torch.float32, device=dev)) for _ in range(rotate)]
+    for x in sets:
+        x["qkv"] = (torch.empty_like(x["xq"]), torch.empty_like(x["xk"]), torch.empty_like(x["xv"]))
+        x["gb"] = (torch.empty((T, H), dtype=torch.float32, device=dev),
+                   torch.empty((T, H), dtype=torch.float32, device=dev))
+        x["st_out"] = torch.empty_like(x["st"])
+    wt, bias = f(inp.w), f(inp.bias)
+    ws = torch.empty(gdn.prefill_workspace_bytes(T, 1, H, D, D, gdn.GDN_BF16, gdn.CHUNK_64), dtype=torch.uint8,
+                     device=dev)
+
+    def layer(i):
+        x = sets[i % rotate]
+        gdn.layer_prefill(x["xq"], x["xk"], x["xv"], wt, x["a"], x["b"], gate_bias=bias, conv_state_in=x["st"],
+                          conv_state_out=x["st_out"], activation="silu", out=x["o"], final_state=x["s"],
+                          qkv=x["qkv"], workspace=ws, chunk=gdn.CHUNK_64)
+
+    def two_calls(i):
+        x = sets[i % rotate]
+        q, k, v = x["qkv"]
+        gdn.preprocess(x["xq"], x["xk"], x["xv"], wt, x["a"], x["b"], gate_bias=bias, conv_state_in=x["st"],
+                       conv_state_out=x["st_out"], activation="silu", out=(q, k, v) + x["gb"])
+        gdn.prefill(q, k, v, x["gb"][0], x["gb"][1], initial_state=None, final_state=x["s"], out=x["o"],
+                    workspace=ws, chunk=gdn.CHUNK_64)
+
+    res = []
+    for fn in (layer, two_calls):
+        spin_up(torch, fn)
+        for i in range(warmup):
+            fn(i)
+        res.append(time_block(torch, fn, steps)[0])
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for m in marks:
+        for e in m:
+            e.record()
+    torch.cuda.synchronize()
+    for i, m in enumerate(marks):
+        gdn.prefill_set_marks(m)
+        layer(i)
+    torch.cuda.synchronize()
+    kern = {"k_layer_prep + k_conv_state": mean([m[0].elapsed_time(m[1]) for m in marks]),
+            "k_chunk_chain": mean([m[1].elapsed_time(m[2]) for m in marks])}
+    return res[0], res[1], kern
+
+
+def layer_entry(layer_ms, two_ms, kern):
+    """The whole layer from the raw projections at T = 4096, H = 48."""
+    nbytes = LAYER_BYTES_PER_TOKEN_HEAD * T * H + PRE_BYTES_FIXED + STATE_BYTES_PER_HEAD * H
+    design = nbytes + LAYER_QKV_ROUND_TRIP_PER_TOKEN_HEAD * T * H
+    gbs = nbytes / (layer_ms / 1e3) / 1e9
+    return {"workload": "gdn_layer_prefill: raw projections -> conv (4 taps) + SiLU + L2 norm + gate maps + "
+                        "chunked prefill, T = 4096, H = 48, d = 128, bf16, conv state in/out, zero initial state",
+            "mean_ms": layer_ms, "tokens_per_s_layer": T / (layer_ms / 1e3),
+            "two_calls_mean_ms": two_ms, "two_calls_tokens_per_s_layer": T / (two_ms / 1e3),
+            "kernels_ms": kern,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+                         "bytes_with_qkv_round_trip": design}}
+
+
+def bench_config4(torch, gdn, w, runs):
+    """Long-context prefill: 262,144 tokens (H = 48) as 16 segments of 16,384
+    with the fp32 state carried from each call to the next, in place; inputs
+    resident (all 16 segments).  Returns (sorted per-run ms, tokens)."""
+    dev = "cuda:0"
+    segs = []
+    for seg in w.config4_segments():
+        segs.append((w.to_torch(seg.q, "bf16", dev), w.to_torch(seg.k, "bf16", dev), w.to_torch(seg.v, "bf16", dev),
+                     torch.from_numpy(seg.g).to(dev), torch.from_numpy(seg.beta).to(dev)))
+        del seg
+    n = segs[0][0].shape[0]
+    state = torch.zeros((1, H, D, D), dtype=torch.float32, device=dev)
+    o = torch.empty((n, H, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.prefill_workspace_bytes(n, 1, H, D, D, gdn.GDN_BF16, gdn.CHUNK_64), dtype=torch.uint8,
+                     device=dev)
+
+    def one_run():
+        state.zero_()
+        for q, k, v, g, b in segs:
+            gdn.prefill(q, k, v, g, b, initial_state=state, final_state=state, out=o, workspace=ws,
+                        chunk=gdn.CHUNK_64)
+
+    spin_up(torch, lambda i: one_run())
+    times = []
+    for _ in range(runs):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        one_run()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    return sorted(times), n * len(segs)
+
+
+def bench_config5(torch, gdn, w, steps, warmup):
+    """Variable-length packed prefill: 8 sequences (130,093 tokens), H = 48,
+    per-sequence initial states; back-to-back calls timed as a block."""
+    inp = w.config5()
+    dev = "cuda:0"
+    q, k, v = (w.to_torch(x, inp.dtype, dev) for x in (inp.q, inp.k, inp.v))
+    g, b = torch.from_numpy(inp.g).to(dev), torch.from_numpy(inp.beta).to(dev)
+    s0 = torch.from_numpy(inp.s_init).to(dev)
+    cu = inp.cu_seqlens
+    cu_dev = torch.from_numpy(cu).to(dev)
+    N, n_seq = q.shape[0], len(cu) - 1
+    o = torch.empty((N, H, D), dtype=torch.float32, device=dev)
+    s1 = torch.empty_like(s0)
+    ws = torch.empty(gdn.prefill_workspace_bytes(N, n_seq, H, D, D, gdn.GDN_BF16, gdn.CHUNK_64), dtype=torch.uint8,
+                     device=dev)
+    call = lambda i: gdn.prefill(q, k, v, g, b, cu_seqlens=cu, cu_seqlens_device=cu_dev, initial_state=s0,
+                                 final_state=s1, out=o, workspace=ws, chunk=gdn.CHUNK_64)
+    spin_up(torch, call)
+    for i in range(warmup):
+        call(i)
+    return time_block(torch, call, steps)[0], N, n_seq
+
+
+def bench_fp32(torch, gdn, w, steps):
+    """fp32 q/k/v at the one-layer shape (T = 4096, H = 48, d = 128): the
+    token-serial kernel (the chunked kernels take bf16)."""
+    inp = w.make_prefill([T], H=H, d=D, dtype="fp32", seed=w.SEED_BASE + 2, packed=False)
+    dev = "cuda:0"
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (inp.q, inp.k, inp.v))
+    g, b = torch.from_numpy(inp.g).to(dev), torch.from_numpy(inp.beta).to(dev)
+    o = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    st = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    call = lambda i: gdn.prefill(q, k, v, g, b, out=o, final_state=st)
+    assert gdn.prefill_algorithm(gdn.GDN_FP32, D, D) == gdn.CHUNK_SERIAL
+    spin_up(torch, call)
+    return time_block(torch, call, steps)[0]
+
+
+def bench_plan(torch, gdn, w, reps):
+    """Packed batches of 1,024 and 4,096 short sequences (H = 2): the planning
+    kernel's cost shows in a kernel trace of this part."""
+    import numpy as np
+    dev = "cuda:0"
+    out = {}
+    for n_seq in (1024, 4096):
+        lengths = np.random.default_rng(n_seq).integers(1, 200, size=n_seq).tolist()
+        inp = w.make_prefill(lengths, H=2, d=D, seed=w.SEED_BASE + 9)
+        q, k, v = (w.to_torch(x, "bf16", dev) for x in (inp.q, inp.k, inp.v))
+        g, b = torch.from_numpy(inp.g).to(dev), torch.from_numpy(inp.beta).to(dev)
+        cu_dev = torch.from_numpy(inp.cu_seqlens).to(dev)
+        call = lambda i: gdn.prefill(q, k, v, g, b, cu_seqlens=inp.cu_seqlens, cu_seqlens_device=cu_dev,
+                                     chunk=gdn.CHUNK_64)
+        call(0)
+        out[f"n_seq_{n_seq}_call_ms"] = time_block(torch, call, reps)[0]
+    return out
+
+
 def bench_copy(torch, gdn, mib, reps):
     """Calibration run for the HBM byte counters: gdn_state_init copying a
     state of about `mib` MiB (k_state_fill reads and writes each byte once)."""
@@ -401,6 +569,37 @@ def pre_entry(pre_block_ms, pre_ms):
                          "algorithmic_bytes": nbytes, "traffic": load_traffic("k_preprocess")}}
 
 
+def long_entry(run_ms, tokens):
+    """Config 4: 16 calls of 16,384 tokens, the state carried (read and written by each call)."""
+    nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * tokens * H + 16 * 2 * STATE_BYTES_PER_HEAD * H
+    ms = mean(run_ms)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": "262,144 tokens as 16 segments of 16,384, H = 48, d = 128, bf16, fp32 state carried "
+                        "in place; 3 full runs", "run_ms": run_ms, "mean_ms": ms,
+            "tokens_per_s_layer": tokens / (ms / 1e3), "hbm_floor_ms": nbytes / (HBM_PEAK_GBS * 1e9) * 1e3,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+
+
+def varlen_entry(ms, tokens, n_seq):
+    """Config 5: one call over the packed batch, initial and final states per sequence."""
+    nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * tokens * H + n_seq * 2 * STATE_BYTES_PER_HEAD * H
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": f"{n_seq} packed sequences, log-uniform lengths in [1024, 65536] ({tokens} tokens), H = 48, "
+                        "d = 128, bf16, per-sequence initial states", "mean_ms": ms,
+            "tokens_per_s_layer": tokens / (ms / 1e3), "hbm_floor_ms": nbytes / (HBM_PEAK_GBS * 1e9) * 1e3,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+
+
+def fp32_entry(ms):
+    """fp32 q/k/v at T = 4096, H = 48: the token-serial kernel."""
+    nbytes = (3 * D * 4 + 2 * 4 + D * 4) * T * H + 2 * STATE_BYTES_PER_HEAD * H
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": "B = 1, H = 48, T = 4096, d = 128, fp32 q/k/v (token-serial kernel)", "mean_ms": ms,
+            "tokens_per_s_layer": T / (ms / 1e3), "achieved_gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,15 +609,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of parts to time alone (prefill, decode, decode_slots, preprocess, scan, copy), one JSON "
-                         "line "
-                         "each, for "
-                         "profiling runs; 'copy' is the byte-counter calibration copy")
+                    help="comma list of parts to time alone (prefill, decode, decode_slots, preprocess, scan, config4, "
+                         "config5, fp32, plan, layer, copy), one JSON line each, for profiling runs; 'copy' is the "
+                         "byte-counter calibration copy")
     ap.add_argument("--warm", action="store_true",
                     help="also time one resident copy (inputs and state may then sit in the last-level cache)")
     ap.add_argument("--rotate", type=int, default=4,
                     help="resident copies of the inputs/states cycled through by successive steps")
     ap.add_argument("--copy-mib", type=float, default=1024.0, help="size of the calibration copy")
+    ap.add_argument("--config4-runs", type=int, default=3, help="full 16-segment runs of the long-context prefill")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the recurrence shards across heads and sequences with no "
@@ -435,7 +634,8 @@ def main():
 
     if args.only:
         parts = args.only.split(",")
-        bad = [p for p in parts if p not in ("prefill", "decode", "decode_slots", "preprocess", "scan", "copy")]
+        bad = [p for p in parts if p not in ("prefill", "decode", "decode_slots", "preprocess", "scan", "copy",
+                                             "config4", "config5", "fp32", "plan", "layer")]
         if bad:
             ap.error(f"--only: unknown part(s) {bad}")
         for part in parts:
@@ -458,6 +658,20 @@ def main():
                 pre_block, pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
                 print(json.dumps({"only": "preprocess", "ms_per_call": pre_block,
                                   "event_bracketed_mean_ms": mean(pre_ms)}), flush=True)
+            elif part == "config4":
+                c4_ms, c4_tok = bench_config4(torch, gdn, w, args.config4_runs)
+                print(json.dumps({"only": "config4", "run_ms": c4_ms, "tokens": c4_tok}), flush=True)
+            elif part == "config5":
+                c5_ms, c5_tok, _ = bench_config5(torch, gdn, w, args.steps, args.warmup)
+                print(json.dumps({"only": "config5", "ms_per_call": c5_ms, "tokens": c5_tok}), flush=True)
+            elif part == "fp32":
+                print(json.dumps({"only": "fp32", "ms_per_call": bench_fp32(torch, gdn, w, max(3, args.steps // 10))}),
+                      flush=True)
+            elif part == "plan":
+                print(json.dumps({"only": "plan", **bench_plan(torch, gdn, w, max(3, args.steps))}), flush=True)
+            elif part == "layer":
+                print(json.dumps({"only": "layer", **layer_entry(*bench_layer(torch, gdn, w, args.steps, args.warmup,
+                                                                             args.rotate))}), flush=True)
             else:
                 print(json.dumps(bench_copy(torch, gdn, args.copy_mib, max(1, args.steps))), flush=True)
         return
@@ -466,6 +680,10 @@ def main():
     pre_block, pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
     (ds_block, ds_ms), (dg_block, dg_ms) = bench_decode_slots(torch, gdn, w, args.decode_steps, args.rotate)
     scan = bench_scan(torch, gdn, w, min(args.steps, 20), args.warmup)
+    c4_ms, c4_tok = bench_config4(torch, gdn, w, args.config4_runs)
+    c5_ms, c5_tok, c5_nseq = bench_config5(torch, gdn, w, min(args.steps, 20), args.warmup)
+    fp32_ms = bench_fp32(torch, gdn, w, 5)
+    layer_ms, layer_two_ms, layer_kern = bench_layer(torch, gdn, w, args.steps, args.warmup, args.rotate)
 
     step_ms = block_ms
     tok_s = T / (step_ms / 1e3)
@@ -541,6 +759,10 @@ def main():
                          "workload": "config-3 step, 64 rows on a permutation of 64 of 128 pool slots; eager "
                                      "launches, and replays of one captured HIP graph holding one step per pool "
                                      "(per-step time = replay time / pools); each timed as a block"},
+        "config4": long_entry(c4_ms, c4_tok),
+        "config5": varlen_entry(c5_ms, c5_tok, c5_nseq),
+        "fp32_prefill": fp32_entry(fp32_ms),
+        "layer": layer_entry(layer_ms, layer_two_ms, layer_kern),
         "rotate": args.rotate,
         "conditions": run_conditions(torch),
     }

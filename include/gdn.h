@@ -7,10 +7,9 @@
  *
  * Source: "Qwen3.8-27B 架构深读: Gated DeltaNet 混合线性注意力与 262K 长上下文"
  * (feifeigd.github.io, 2026-08-17), section 三 (Gated DeltaNet): the gated
- * delta-rule equation and the single-step sketch (recall with the key from the
- * ungated state, gate the state, write the correction along the key).  The
- * read-out o_t = S_t q_t is the page's linear-attention read-out applied to the
- * updated state.  The same section says training accumulates the state chunk
+ * delta-rule equation, whose error term v_t - S_{t-1} k_t reads the state
+ * before the gate.  The read-out o_t = S_t q_t is the page's linear-attention
+ * read-out applied to the updated state.  The same section says training accumulates the state chunk
  * by chunk in parallel while inference does one fixed-size matrix update per
  * step: gdn_prefill and gdn_decode_step are those two modes.
  *
@@ -49,10 +48,16 @@
 extern "C" {
 #endif
 
-/* Element type of q, k and v.  g, beta, states and o are always fp32. */
-typedef enum { GDN_BF16 = 0, GDN_FP32 = 1 } gdn_dtype;
+/* Element type of q, k and v.  g, beta, states and o are always fp32.  The
+ * type is a plain 32-bit integer (not an enum), so that any value a caller
+ * passes is a valid argument: unknown values return GDN_ERR_DTYPE. */
+typedef int32_t gdn_dtype;
+enum { GDN_BF16 = 0, GDN_FP32 = 1 };
 
-typedef enum {
+/* Status of every call: GDN_OK or one of the error codes below (a plain
+ * 32-bit integer, for the same reason). */
+typedef int32_t gdn_status;
+enum {
     GDN_OK = 0,
     GDN_ERR_NULL = 1,        /* a required pointer is NULL */
     GDN_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree */
@@ -64,7 +69,7 @@ typedef enum {
     GDN_ERR_ALIAS = 8,       /* an output overlaps an input it must not overlap */
     GDN_ERR_HIP = 9,         /* the HIP runtime reported an error */
     GDN_ERR_SLOTS = 10       /* a state slot out of range, or one slot used twice in a batch */
-} gdn_status;
+};
 
 /* Prefill algorithms (the `chunk` argument of gdn_prefill). */
 #define GDN_CHUNK_AUTO 0     /* chunked (64) where built, else token-serial */
@@ -219,8 +224,8 @@ gdn_status gdn_decode_step_slots(const void *q, const void *k, const void *v, gd
                                  const int32_t *slots, const int32_t *slots_host, float *o,
                                  int64_t B, int32_t H, int32_t dk, int32_t dv, int32_t variant, void *stream);
 
-/* Activation after the pre-processing convolution. */
-typedef enum { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_activation;
+/* Activation after the pre-processing convolution (the `activation` argument). */
+enum { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 };
 
 /* Pre-processing in front of the recurrence, for a packed batch laid out as
  * for gdn_prefill.  The DeltaNet layers of "Layouts híbridos: três DeltaNet,
@@ -259,6 +264,42 @@ gdn_status gdn_preprocess(const void *xq, const void *xk, const void *xv, gdn_dt
                           int64_t total_tokens, int32_t H, int32_t d, int32_t activation,
                           void *q, void *k, void *v, float *g, float *beta, void *stream);
 
+/* The layer's recurrence from its raw projections: gdn_preprocess and
+ * gdn_prefill in one pass over the raw inputs.  The DeltaNet layers of
+ * "Layouts híbridos: três DeltaNet, uma attention" (llmdeepdive.com), section
+ * Conceito, carry a convolution of kernel 4 beside their gated state; the
+ * gated delta rule and its per-token gate and strength are those of
+ * "Qwen3.8-27B 架构深读" (feifeigd.github.io, 2026-08-17), section 三.
+ * The chunk preparation forms the convolution, activation, L2 norm of q and
+ * k, and the gate maps exactly as gdn_preprocess does (the same bits), writes
+ * the processed q, k, v once, and the state chain reads them back: the
+ * outputs equal gdn_preprocess followed by gdn_prefill (chunked), bit for bit.
+ *
+ *   xq, xk, xv, conv_w, conv_state_in, conv_state_out, activation, a_logit,
+ *   b_logit, gate_bias     as for gdn_preprocess (conv_state_out required;
+ *                          a_logit ignored, and may be NULL, with GDN_VARIANT_NO_GATE)
+ *   cu_seqlens, cu_seqlens_host, n_seq, total_tokens, H, initial_state, o,
+ *   final_state, chunk, workspace, workspace_bytes, variant
+ *                          as for gdn_prefill (chunk: GDN_CHUNK_AUTO or one of
+ *                          the GDN_CHUNK_64 forms; the workspace size is
+ *                          gdn_prefill_workspace_bytes(..., GDN_BF16, chunk))
+ *   q, k, v    [N][H][d] bf16 outputs: the processed inputs of the recurrence
+ *              (caller-owned; the state chain reads them)
+ *   g, beta    [N][H] fp32 outputs, or NULL when not wanted
+ * Only bf16 with d = 128 (the chunked prefill) is built: anything else is
+ * GDN_ERR_UNSUPPORTED (use gdn_preprocess, then gdn_prefill).  No output may
+ * overlap an input or another output, except conv_state_out == conv_state_in
+ * and final_state == initial_state (updated in place).  Errors as for the
+ * other calls. */
+gdn_status gdn_layer_prefill(const void *xq, const void *xk, const void *xv, gdn_dtype dtype,
+                             const float *conv_w, const void *conv_state_in, void *conv_state_out,
+                             int32_t activation, const float *a_logit, const float *b_logit,
+                             const float *gate_bias, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                             int64_t n_seq, int64_t total_tokens, int32_t H, int32_t d,
+                             const float *initial_state, float *o, float *final_state,
+                             void *q, void *k, void *v, float *g, float *beta, int32_t chunk,
+                             void *workspace, size_t workspace_bytes, int32_t variant, void *stream);
+
 /* Profiling hook.  Arms up to three caller-owned hipEvent_t handles
  * (events[0..n_events-1]; NULL entries are skipped) for the NEXT gdn_prefill
  * call made by this host thread, which records them on its stream:
@@ -271,7 +312,7 @@ gdn_status gdn_preprocess(const void *xq, const void *xk, const void *xv, gdn_dt
  * GDN_ERR_NULL for a NULL array with n_events > 0 (the hook is then disarmed). */
 gdn_status gdn_prefill_set_marks(void *const *events, int32_t n_events);
 
-/* Static description of a status code. */
+/* Static description of a status code ("unknown status" for any other value). */
 const char *gdn_status_string(gdn_status status);
 
 /* Detail of the last failing call made by the calling thread ("" if none). */

@@ -299,6 +299,124 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
                       "prefill (serial) launch");
 }
 
+gdn_status gdn_layer_prefill(const void *xq, const void *xk, const void *xv, gdn_dtype dtype, const float *conv_w,
+                             const void *conv_state_in, void *conv_state_out, int32_t activation,
+                             const float *a_logit, const float *b_logit, const float *gate_bias,
+                             const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
+                             int64_t total_tokens, int32_t H, int32_t d, const float *initial_state, float *o,
+                             float *final_state, void *q, void *k, void *v, float *g, float *beta, int32_t chunk,
+                             void *workspace, size_t workspace_bytes, int32_t variant, void *stream) {
+    const Marks marks = take_marks();
+    if (dtype != GDN_BF16 && dtype != GDN_FP32) return fail(GDN_ERR_DTYPE, "layer_prefill: dtype %d", (int)dtype);
+    if (variant & ~GDN_VARIANT_MASK) return fail(GDN_ERR_UNSUPPORTED, "layer_prefill: variant %d", variant);
+    if (variant & GDN_VARIANT_NO_GATE) a_logit = nullptr;  // ignored: the ungated rule
+    if (n_seq < 0 || total_tokens < 0 || H <= 0 || total_tokens > (int64_t)INT32_MAX)
+        return fail(GDN_ERR_SHAPE, "layer_prefill: n_seq=%lld total_tokens=%lld H=%d", (long long)n_seq,
+                    (long long)total_tokens, H);
+    if (activation != GDN_ACT_NONE && activation != GDN_ACT_SILU)
+        return fail(GDN_ERR_UNSUPPORTED, "layer_prefill: activation %d", activation);
+    const int32_t algo = pick_algorithm(dtype, d, d, chunk);
+    if (!is_chunked(algo) || dtype != GDN_BF16 || d != 128)
+        return fail(GDN_ERR_UNSUPPORTED,
+                    "layer_prefill: the fused layer runs the chunked algorithm on bf16 with d = 128 (dtype=%d d=%d "
+                    "chunk=%d); use gdn_preprocess and gdn_prefill",
+                    (int)dtype, d, chunk);
+    if (!gdn::prefill_chunked_fits(total_tokens, n_seq, H))
+        return fail(GDN_ERR_SHAPE, "layer_prefill: n_seq=%lld total_tokens=%lld H=%d exceed one launch",
+                    (long long)n_seq, (long long)total_tokens, H);
+    if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr))
+        return fail(GDN_ERR_NULL, "layer_prefill: cu_seqlens and cu_seqlens_host must both be given or both be NULL");
+    if (!cu_seqlens) {
+        if (n_seq != 1)
+            return fail(GDN_ERR_SEQLENS, "layer_prefill: without cu_seqlens n_seq must be 1 (got %lld)",
+                        (long long)n_seq);
+    } else {
+        if (!aligned(cu_seqlens, 4)) return fail(GDN_ERR_ALIGN, "layer_prefill: cu_seqlens must be 4-byte aligned");
+        if (cu_seqlens_host[0] != 0)
+            return fail(GDN_ERR_SEQLENS, "layer_prefill: cu_seqlens[0] = %d", cu_seqlens_host[0]);
+        for (int64_t s = 0; s < n_seq; ++s)
+            if (cu_seqlens_host[s + 1] < cu_seqlens_host[s])
+                return fail(GDN_ERR_SEQLENS, "layer_prefill: cu_seqlens decreases at %lld", (long long)s);
+        if ((int64_t)cu_seqlens_host[n_seq] != total_tokens)
+            return fail(GDN_ERR_SEQLENS, "layer_prefill: cu_seqlens[n_seq] = %d but total_tokens = %lld",
+                        cu_seqlens_host[n_seq], (long long)total_tokens);
+    }
+    if (n_seq == 0) return ok();
+    const size_t sbytes = gdn_state_bytes(n_seq, H, d, d);
+    if (sbytes == 0) return fail(GDN_ERR_SHAPE, "layer_prefill: state size overflows");
+    if (!final_state || !conv_state_out) return fail(GDN_ERR_NULL, "layer_prefill: final_state and conv_state_out are required");
+    if (total_tokens > 0 && (!xq || !xk || !xv || !conv_w || (!a_logit && !(variant & GDN_VARIANT_NO_GATE)) ||
+                             !b_logit || !o || !q || !k || !v))
+        return fail(GDN_ERR_NULL, "layer_prefill: xq, xk, xv, conv_w, the logits, o, q, k and v are required");
+    for (const void *p : {xq, xk, xv, (const void *)q, (const void *)k, (const void *)v, conv_state_in,
+                          (const void *)conv_state_out, (const void *)conv_w, (const void *)o,
+                          (const void *)initial_state, (const void *)final_state})
+        if (p && !aligned(p, 16)) return fail(GDN_ERR_ALIGN, "layer_prefill: tensors and states must be 16-byte aligned");
+    if (!aligned(a_logit, 4) || !aligned(b_logit, 4) || !aligned(gate_bias, 4) || !aligned(g, 4) || !aligned(beta, 4))
+        return fail(GDN_ERR_ALIGN, "layer_prefill: logits, bias and gates must be 4-byte aligned");
+    const size_t NH = (size_t)total_tokens * H, xb = NH * d * 2, cb = (size_t)n_seq * 9 * H * d * 2;
+    const Range in[] = {{xq, xb}, {xk, xb}, {xv, xb}, {conv_w, (size_t)12 * H * d * 4}, {a_logit, NH * 4},
+                        {b_logit, NH * 4}, {gate_bias, (size_t)H * 4},
+                        {cu_seqlens, cu_seqlens ? (size_t)(n_seq + 1) * 4 : 0}, {conv_state_in, cb},
+                        {initial_state, initial_state ? sbytes : 0}};
+    const Range out[] = {{o, NH * d * 4}, {q, xb}, {k, xb}, {v, xb}, {g, NH * 4}, {beta, NH * 4}};
+    const Range rso{conv_state_out, cb}, rs1{final_state, sbytes};
+    for (const Range &a : out) {
+        for (const Range &i : in)
+            if (overlap(a, i)) return fail(GDN_ERR_ALIAS, "layer_prefill: an output overlaps an input");
+        for (const Range &b : out)
+            if (&b != &a && overlap(a, b)) return fail(GDN_ERR_ALIAS, "layer_prefill: outputs overlap");
+        if (overlap(a, rso) || overlap(a, rs1)) return fail(GDN_ERR_ALIAS, "layer_prefill: outputs overlap");
+    }
+    for (const Range &i : in) {
+        if (i.p != conv_state_in && overlap(rso, i))
+            return fail(GDN_ERR_ALIAS, "layer_prefill: conv_state_out overlaps an input");
+        if (i.p != initial_state && overlap(rs1, i))
+            return fail(GDN_ERR_ALIAS, "layer_prefill: final_state overlaps an input");
+    }
+    if (overlap(rso, rs1)) return fail(GDN_ERR_ALIAS, "layer_prefill: conv_state_out overlaps final_state");
+    if (conv_state_in && conv_state_in != conv_state_out && overlap(rso, Range{conv_state_in, cb}))
+        return fail(GDN_ERR_ALIAS, "layer_prefill: conv_state_in partially overlaps conv_state_out");
+    if (initial_state && initial_state != final_state && overlap(rs1, Range{initial_state, sbytes}))
+        return fail(GDN_ERR_ALIAS, "layer_prefill: initial_state partially overlaps final_state");
+    if (algo == GDN_CHUNK_64_SCAN && !gdn::prefill_chunked_scan_supported(n_seq, total_tokens))
+        return fail(GDN_ERR_UNSUPPORTED,
+                    "layer_prefill: the chunk-level scan takes 1 to 64 sequences and at least one token");
+    const size_t need = gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H, chunked_mode(algo));
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GDN_ERR_WORKSPACE, "layer_prefill: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (workspace && !aligned(workspace, 256))
+        return fail(GDN_ERR_ALIGN, "layer_prefill: workspace must be 256-byte aligned");
+    for (const Range &i : in)
+        if (overlap({workspace, need}, i)) return fail(GDN_ERR_ALIAS, "layer_prefill: workspace overlaps an argument");
+    for (const Range &a : out)
+        if (overlap({workspace, need}, a)) return fail(GDN_ERR_ALIAS, "layer_prefill: workspace overlaps an argument");
+    if (overlap({workspace, need}, rso) || overlap({workspace, need}, rs1))
+        return fail(GDN_ERR_ALIAS, "layer_prefill: workspace overlaps an argument");
+    gdn::LayerRaw raw;
+    raw.xq = static_cast<const uint16_t *>(xq);
+    raw.xk = static_cast<const uint16_t *>(xk);
+    raw.xv = static_cast<const uint16_t *>(xv);
+    raw.w = conv_w;
+    raw.st_in = static_cast<const uint16_t *>(conv_state_in);
+    raw.st_out = static_cast<uint16_t *>(conv_state_out);
+    raw.a_logit = a_logit;
+    raw.b_logit = b_logit;
+    raw.bias = gate_bias;
+    raw.act = activation;
+    raw.q = static_cast<uint16_t *>(q);
+    raw.k = static_cast<uint16_t *>(k);
+    raw.v = static_cast<uint16_t *>(v);
+    raw.g = g;
+    raw.beta = beta;
+    return hip_status(gdn::launch_prefill_chunked(q, k, v, nullptr, nullptr, cu_seqlens, cu_seqlens_host, n_seq,
+                                                  total_tokens, H, initial_state, o, final_state, workspace,
+                                                  erase_of(variant), chunked_mode(algo), marks.ev,
+                                                  (hipStream_t)stream, &raw),
+                      "layer_prefill launch");
+}
+
 gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v, gdn_dtype dtype, const float *g,
                                const float *beta, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                                int64_t n_seq, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,

@@ -62,6 +62,7 @@
 #include <algorithm>
 #include <cfloat>
 
+#include "gdn_conv.h"
 #include "gdn_device.h"
 #include "gdn_launch.h"
 #include "gdn_mfma.h"
@@ -324,44 +325,85 @@ __device__ __forceinline__ u32x4_t colfrag_st(const char *tile, int ks, int cm, 
 }
 
 // ---------------------------------------------------------------------------
-// k_plan: chunk_base[s] = sum over earlier sequences of ceil(len / 64);
-// seq_order lists sequences by decreasing length (ties by index) when n_seq <= 4096.
-__global__ __launch_bounds__(256) void k_plan(const int32_t *__restrict__ cu, int n_seq, int32_t *__restrict__ chunk_base,
-                                              int32_t *__restrict__ seq_order) {
-    __shared__ int32_t part[256];
-    __shared__ int32_t carry_s;
-    const int tid = threadIdx.x;
-    if (tid == 0) carry_s = 0;
+// k_plan: chunk_base[s] = sum over earlier sequences of ceil(len / 64), and
+// seq_order, the sequences longest first (by chunk count; sequences of 4,095
+// chunks or more count as 4,095).  The order only decides which workgroups
+// take which (sequence, head) pairs, a longest-first schedule: every pair does
+// the same arithmetic wherever it runs, so any order gives the same results,
+// and equal chunk counts may come out in any order.  A counting sort: a
+// histogram of the counts in LDS, its prefix sum, then each sequence takes the
+// next slot of its count.
+constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_BINS = 4096;
+
+// Inclusive sum of x over the workgroup's threads (tid order); wsum: 16 ints of LDS.
+__device__ __forceinline__ int block_inclusive_scan(int x, int tid, int *wsum) {
+    const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
     __syncthreads();
-    for (int base = 0; base < n_seq; base += 256) {
+    if (wv == 0) {
+        int t = lane < PLAN_THREADS / 64 ? wsum[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < PLAN_THREADS / 64; off <<= 1) {
+            const int y = __shfl_up(t, off, 64);
+            if (lane >= off) t += y;
+        }
+        if (lane < PLAN_THREADS / 64) wsum[lane] = t;
+    }
+    __syncthreads();
+    const int r = x + (wv > 0 ? wsum[wv - 1] : 0);
+    __syncthreads();  // wsum may be reused
+    return r;
+}
+
+__global__ __launch_bounds__(PLAN_THREADS) void k_plan(const int32_t *__restrict__ cu, int n_seq,
+                                                       int32_t *__restrict__ chunk_base,
+                                                       int32_t *__restrict__ seq_order) {
+    __shared__ int32_t bins[PLAN_BINS];
+    __shared__ int32_t wsum[PLAN_THREADS / 64];
+    const int tid = threadIdx.x;
+    constexpr int PER = PLAN_BINS / PLAN_THREADS;
+    __shared__ int32_t round_total;
+    for (int i = tid; i < PLAN_BINS; i += PLAN_THREADS) bins[i] = 0;
+    __syncthreads();
+    // chunk offsets in sequence order, PLAN_THREADS sequences per round, and the histogram
+    int carry = 0;
+    for (int base = 0; base < n_seq; base += PLAN_THREADS) {
         const int s = base + tid;
         const int cnt = s < n_seq ? (cu[s + 1] - cu[s] + C - 1) / C : 0;
-        part[tid] = cnt;
+        if (s < n_seq) atomicAdd(&bins[PLAN_BINS - 1 - min(cnt, PLAN_BINS - 1)], 1);
+        const int inc = block_inclusive_scan(cnt, tid, wsum);
+        if (s < n_seq) chunk_base[s] = carry + inc - cnt;
+        if (tid == PLAN_THREADS - 1) round_total = inc;  // the round's total
         __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-            const int y = tid >= off ? part[tid - off] : 0;
-            __syncthreads();
-            part[tid] += y;
-            __syncthreads();
-        }
-        const int carry = carry_s;
-        if (s < n_seq) chunk_base[s] = carry + part[tid] - cnt;
-        __syncthreads();
-        if (tid == 255) carry_s = carry + part[255];
+        carry += round_total;
         __syncthreads();
     }
-    if (tid == 0) chunk_base[n_seq] = carry_s;
-    for (int s = tid; s < n_seq; s += 256) {
-        int rank = s;
-        if (n_seq <= 4096) {
-            const int L = cu[s + 1] - cu[s];
-            rank = 0;
-            for (int s2 = 0; s2 < n_seq; ++s2) {
-                const int L2 = cu[s2 + 1] - cu[s2];
-                rank += (L2 > L) || (L2 == L && s2 < s);
-            }
-        }
-        seq_order[rank] = s;
+    if (tid == 0) chunk_base[n_seq] = carry;
+    // exclusive prefix sum over the bins (PER consecutive bins per thread)
+    int local[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        local[j] = bins[PER * tid + j];
+        sum += local[j];
+    }
+    const int excl = block_inclusive_scan(sum, tid, wsum) - sum;
+    int run = excl;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        bins[PER * tid + j] = run;
+        run += local[j];
+    }
+    __syncthreads();
+    for (int s = tid; s < n_seq; s += PLAN_THREADS) {
+        const int cnt = (cu[s + 1] - cu[s] + C - 1) / C;
+        const int pos = atomicAdd(&bins[PLAN_BINS - 1 - min(cnt, PLAN_BINS - 1)], 1);
+        seq_order[pos] = s;
     }
 }
 
@@ -393,46 +435,14 @@ struct ScanSegs {
     int32_t h_cu[SCAN_MAX_SEGMENTS + 1], h_base[SCAN_MAX_SEGMENTS + 1], h_seg0[SCAN_MAX_SEGMENTS + 1];
 };
 
-__global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                                    const float *__restrict__ g, const float *__restrict__ beta,
-                                                    const int32_t *__restrict__ cu,
-                                                    const int32_t *__restrict__ chunk_base, int n_seq,
-                                                    int64_t total_tokens, int H, int erase,
-                                                    char *__restrict__ recs, ScanSegs segs) {
-    if (blockIdx.x == 0 && segs.cu) {
-        for (int i = threadIdx.x; i <= segs.P; i += 256) {
-            segs.cu[i] = segs.h_cu[i];
-            segs.base[i] = segs.h_base[i];
-        }
-        for (int i = threadIdx.x; i <= segs.n_seq; i += 256) segs.seg0[i] = segs.h_seg0[i];
-    }
-    const int64_t gc = blockIdx.x / H;
-    const int h = blockIdx.x % H;
-    int64_t t0;
-    int n;
-    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, t0, n);
-    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
-    char *rec = recs + (gc * H + h) * (int64_t)REC_BYTES;
-    const int64_t rs = (int64_t)H * DK;
-    const int64_t cbase = (t0 * H + h) * DK;
-
-    __shared__ PrepSmem S;
-
-    // the gates first (wave 0), so that their scan overlaps the row copies
-    float gl = 1.f, bl = 0.f;
-    if (wave == 0) {  // unconditional loads (no g: beta's value stands in and is not used)
-        const int64_t off = (t0 + min(lane, n - 1)) * H + h;
-        gl = (g ? g : beta)[off];
-        bl = beta[off];
-    }
-    // q, k rows of the chunk -> LDS row tiles (8 one-kilobyte copies per wave)
-    dma_rows(S.KL, k + cbase, rs, n, lane, wave, 4);
-    dma_rows(S.QT, q + cbase, rs, n, lane, wave, 4);
-    asm volatile("" : "+v"(gl), "+v"(bl));  // keeps the gate arithmetic after the copies are issued
+// Everything of a chunk's preparation once its q and k rows are on their way
+// into (or in) the row tiles S.QT and S.KL: wave 0 holds the chunk's gates gl
+// (g, unless has_g is false) and bl (beta) for token min(lane, n - 1).
+__device__ __forceinline__ void prep_body(PrepSmem &S, char *__restrict__ rec, int n, float gl, float bl, bool has_g,
+                                          int erase, int wave, int lane, int g4, int r) {
     float f_eg = 0.f, f_egm1 = 0.f, f_egn = 0.f;  // the record's gate factors (wave 0)
     if (wave == 0) {  // gate prefix sums
-        const float lam = (lane < n && g) ? __logf(fmaxf(gl, FLT_MIN)) : 0.f;
+        const float lam = (lane < n && has_g) ? __logf(fmaxf(gl, FLT_MIN)) : 0.f;
         const float bt = lane < n ? bl : 0.f;
         const float G = wave_inclusive_scan(lam, lane);
         const float Gm1 = __shfl_up(G, 1, 64);
@@ -664,6 +674,159 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
             }
         }
     }
+}
+
+__global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                    const float *__restrict__ g, const float *__restrict__ beta,
+                                                    const int32_t *__restrict__ cu,
+                                                    const int32_t *__restrict__ chunk_base, int n_seq,
+                                                    int64_t total_tokens, int H, int erase,
+                                                    char *__restrict__ recs, ScanSegs segs) {
+    if (blockIdx.x == 0 && segs.cu) {
+        for (int i = threadIdx.x; i <= segs.P; i += 256) {
+            segs.cu[i] = segs.h_cu[i];
+            segs.base[i] = segs.h_base[i];
+        }
+        for (int i = threadIdx.x; i <= segs.n_seq; i += 256) segs.seg0[i] = segs.h_seg0[i];
+    }
+    const int64_t gc = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    int64_t t0;
+    int n;
+    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, t0, n);
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
+    char *rec = recs + (gc * H + h) * (int64_t)REC_BYTES;
+    const int64_t rs = (int64_t)H * DK;
+    const int64_t cbase = (t0 * H + h) * DK;
+
+    __shared__ PrepSmem S;
+
+    // the gates first (wave 0), so that their scan overlaps the row copies
+    float gl = 1.f, bl = 0.f;
+    if (wave == 0) {  // unconditional loads (no g: beta's value stands in and is not used)
+        const int64_t off = (t0 + min(lane, n - 1)) * H + h;
+        gl = (g ? g : beta)[off];
+        bl = beta[off];
+    }
+    // q, k rows of the chunk -> LDS row tiles (8 one-kilobyte copies per wave)
+    dma_rows(S.KL, k + cbase, rs, n, lane, wave, 4);
+    dma_rows(S.QT, q + cbase, rs, n, lane, wave, 4);
+    asm volatile("" : "+v"(gl), "+v"(bl));  // keeps the gate arithmetic after the copies are issued
+    prep_body(S, rec, n, gl, bl, g != nullptr, erase, wave, lane, g4, r);
+}
+
+// ---------------------------------------------------------------------------
+// k_layer_prep: the chunk preparation of the fused layer, one 4-wave
+// workgroup per (global chunk, head), from the raw projections.  The
+// pre-processing of "Layouts híbridos: três DeltaNet, uma attention"
+// (llmdeepdive.com), section Conceito (a convolution of kernel 4 beside the
+// gated state) and the per-token gate and strength of "Qwen3.8-27B 架构深读",
+// section 三, formed here with the per-row arithmetic of gdn_preprocess (the
+// same bits): for each of q, k, v a thread owns 8 channels of 4 consecutive
+// rows (16 lanes per row), loads the 7 raw rows of its window once (the 3 rows
+// before a sequence's first token come from its conv state, or are zero),
+// and writes the processed rows to the caller's q, k, v and, for q and k, to
+// the row tiles; wave 0 maps the gates.  The rest is the chunk preparation.
+// Rows past the chunk's end are formed from clamped windows: any finite
+// values do there (see the header of this file), and they are not stored.
+// The returned conv state is written afterwards by k_conv_state.
+__global__ __launch_bounds__(256, 4) void k_layer_prep(LayerRaw raw, const int32_t *__restrict__ cu,
+                                                    const int32_t *__restrict__ chunk_base, int n_seq,
+                                                    int64_t total_tokens, int H, int erase, int has_g,
+                                                    char *__restrict__ recs, ScanSegs segs) {
+    if (blockIdx.x == 0 && segs.cu) {
+        for (int i = threadIdx.x; i <= segs.P; i += 256) {
+            segs.cu[i] = segs.h_cu[i];
+            segs.base[i] = segs.h_base[i];
+        }
+        for (int i = threadIdx.x; i <= segs.n_seq; i += 256) segs.seg0[i] = segs.h_seg0[i];
+    }
+    const int64_t gc = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    int64_t t0;
+    int n;
+    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, t0, n);
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
+    char *rec = recs + (gc * H + h) * (int64_t)REC_BYTES;
+    const int64_t rs = (int64_t)H * DK;
+
+    __shared__ PrepSmem S;
+
+    // the gates (wave 0): loads first, so that they overlap the row work
+    float gl = 1.f, bl = 0.f;
+    if (wave == 0) {
+        const int64_t off = (t0 + min(lane, n - 1)) * H + h;
+        const float a = has_g ? raw.a_logit[off] : 0.f, b = raw.b_logit[off];
+        const float bias = raw.bias ? raw.bias[h] : 0.f;
+        gl = gate_g(a, bias);
+        bl = gate_beta(b);
+        if (lane < n) {
+            if (raw.g) raw.g[(t0 + lane) * H + h] = gl;
+            if (raw.beta) raw.beta[(t0 + lane) * H + h] = bl;
+        }
+    }
+
+    // the sequence holding this chunk and the first token of that sequence
+    int sq = 0;
+    int64_t q0 = 0;
+    if (cu) {
+        int lo = 0, hi = n_seq;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (chunk_base[mid] <= gc) lo = mid; else hi = mid;
+        }
+        sq = lo;
+        q0 = cu[lo];
+    }
+    const int i4 = tid >> 4, lr = tid & 15;  // rows 4 i4 .. 4 i4 + 3, channels 8 lr .. 8 lr + 7
+    using V = Vec8<uint16_t>;
+#pragma unroll 1
+    for (int tau = 0; tau < 3; ++tau) {
+        const uint16_t *x = (tau == 0 ? raw.xq : tau == 1 ? raw.xk : raw.xv) + (int64_t)h * DK + 8 * lr;
+        float tap[8][4];
+        {
+            const float *wp = raw.w + ((int64_t)(tau * H + h) * DK + 8 * lr) * 4;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float4 f = *reinterpret_cast<const float4 *>(wp + 4 * e);
+                tap[e][0] = f.x; tap[e][1] = f.y; tap[e][2] = f.z; tap[e][3] = f.w;
+            }
+        }
+        // window rows 4 i4 - 3 + m, m = 0..6, clamped to the chunk's last row;
+        // before the sequence's first token: its conv state, or zero
+        typename V::raw_t wr[7];
+#pragma unroll
+        for (int m = 0; m < 7; ++m) {
+            const int64_t p = t0 + min(4 * i4 - 3 + m, n - 1);
+            if (p >= q0) {
+                wr[m] = V::load(x + p * rs);
+            } else if (raw.st_in) {
+                wr[m] = V::load(raw.st_in + ((int64_t)(sq * 3 + tau) * 3 + (3 - (q0 - p))) * rs +
+                                (int64_t)h * DK + 8 * lr);
+            } else {
+                wr[m] = V::zero();
+            }
+        }
+        uint16_t *y = (tau == 0 ? raw.q : tau == 1 ? raw.k : raw.v) + (int64_t)h * DK + 8 * lr;
+        char *tile = tau == 0 ? S.QT : S.KL;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 4 * i4 + j;
+            float w0[8], w1[8], w2[8], cur[8], acc[8];  // the window, unpacked per row
+            V::unpack(wr[j], w0);
+            V::unpack(wr[j + 1], w1);
+            V::unpack(wr[j + 2], w2);
+            V::unpack(wr[j + 3], cur);
+            pre_row<16>(tap, w0, w1, w2, cur, raw.act, tau < 2, acc);
+            const uint32_t p0 = pack_bf16x2(acc[0], acc[1]), p1 = pack_bf16x2(acc[2], acc[3]),
+                           p2 = pack_bf16x2(acc[4], acc[5]), p3 = pack_bf16x2(acc[6], acc[7]);
+            if (t < n) store_nt16(y + (t0 + t) * rs, p0, p1, p2, p3);
+            if (tau < 2) *reinterpret_cast<u32x4_t *>(tile + t * 256 + ((lr ^ (t & 15)) << 4)) = u32x4_t{p0, p1, p2, p3};
+        }
+    }
+    prep_body(S, rec, n, gl, bl, has_g != 0, erase, wave, lane, g4, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -1455,7 +1618,7 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
                                   const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
                                   int64_t total_tokens, int H, const float *initial_state, float *o,
                                   float *final_state, void *workspace, int erase, int mode,
-                                  const hipEvent_t *marks, hipStream_t stream) {
+                                  const hipEvent_t *marks, hipStream_t stream, const LayerRaw *raw) {
     if (!prefill_chunked_fits(total_tokens, n_seq, H)) return hipErrorInvalidConfiguration;
     const WsLayout L = ws_layout(total_tokens, n_seq, H, scan_possible(mode, n_seq, H));
     ScanPlan sp;
@@ -1479,7 +1642,7 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
         }
         for (int64_t s = 0; s < n_seq; ++s)
             n_long += 2 * ((cu_seqlens_host[s + 1] - cu_seqlens_host[s] + C - 1) / C) > max_chunks;
-        hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, stream, cu_seqlens, (int)n_seq, chunk_base, seq_order);
+        hipLaunchKernelGGL(k_plan, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens, (int)n_seq, chunk_base, seq_order);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else {
@@ -1497,10 +1660,20 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
         std::copy(sp.seg0, sp.seg0 + n_seq + 1, segs.h_seg0);
     }
     if (n_chunks > 0) {
-        hipLaunchKernelGGL(k_chunk_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream,
-                           static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), g, beta, cu_seqlens,
-                           chunk_base, (int)n_seq, total_tokens, H, erase, recs, segs);
+        if (raw)
+            hipLaunchKernelGGL(k_layer_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream, *raw, cu_seqlens,
+                               chunk_base, (int)n_seq, total_tokens, H, erase, raw->a_logit != nullptr ? 1 : 0, recs,
+                               segs);
+        else
+            hipLaunchKernelGGL(k_chunk_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream,
+                               static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), g, beta,
+                               cu_seqlens, chunk_base, (int)n_seq, total_tokens, H, erase, recs, segs);
         e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (raw) {  // the returned conv state, after every chunk preparation has read the starting state
+        e = launch_conv_state(true, DK, raw->xq, raw->xk, raw->xv, raw->st_in, raw->st_out, cu_seqlens, n_seq,
+                              total_tokens, H, stream);
         if (e != hipSuccess) return e;
     }
     e = record_mark(marks[1], stream);

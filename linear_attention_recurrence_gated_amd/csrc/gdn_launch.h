@@ -38,6 +38,22 @@ hipError_t launch_prefill_serial(bool bf16, int d, const void *q, const void *k,
                                  const float *initial_state, float *o, float *final_state, int erase,
                                  const hipEvent_t *marks, hipStream_t stream);
 
+// Raw inputs of the fused layer (the pre-processing in front of the chunked
+// prefill, bf16, d = 128): when given to launch_prefill_chunked, its chunk
+// preparation forms q, k, v (into q, k, v, which the chain then reads) and the
+// gates from these, and the returned conv state is written after it.
+struct LayerRaw {
+    const uint16_t *xq, *xk, *xv;     // [N][H][128]
+    const float *w;                   // [3][H][128][4]
+    const uint16_t *st_in;            // [n_seq][3][3][H][128] or NULL (zeros)
+    uint16_t *st_out;                 // [n_seq][3][3][H][128]
+    const float *a_logit, *b_logit;   // [N][H] (a_logit NULL without the gate)
+    const float *bias;                // [H] or NULL
+    int act;                          // 0 none, 1 SiLU
+    uint16_t *q, *k, *v;              // [N][H][128] outputs
+    float *g, *beta;                  // [N][H] outputs, or NULL
+};
+
 // Chunkwise-parallel prefill (64-token chunks, d = 128, bf16 q/k/v).
 // Chunked prefill modes: the library's choice, one chain per (sequence, head),
 // or the chunk-level scan (up to 64 sequences cut into segments).
@@ -50,7 +66,14 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v,
                                   const int32_t *cu_seqlens_host, int64_t n_seq,
                                   int64_t total_tokens, int H, const float *initial_state,
                                   float *o, float *final_state, void *workspace, int erase, int mode,
-                                  const hipEvent_t *marks, hipStream_t stream);
+                                  const hipEvent_t *marks, hipStream_t stream, const LayerRaw *raw = nullptr);
+
+// The returned conv state of the pre-processing: per sequence, tensor, head
+// and channel, the last three raw inputs (shifted in from st_in for a sequence
+// shorter than three).  st_out may be st_in.
+hipError_t launch_conv_state(bool bf16, int d, const void *xq, const void *xk, const void *xv, const void *st_in,
+                             void *st_out, const int32_t *cu, int64_t n_seq, int64_t total_tokens, int H,
+                             hipStream_t stream);
 
 // Pre-processing: conv (4 taps) + optional SiLU + L2 norm of q, k + gate maps,
 // then the returned conv state.

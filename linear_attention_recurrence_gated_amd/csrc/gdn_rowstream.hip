@@ -1,9 +1,10 @@
 // gdn_rowstream.hip -- the two token-at-a-time kernels of the gated delta rule.
 //
-// Both follow the single-step update of "Qwen3.8-27B 架构深读" (feifeigd.github.io,
-// 2026-08-17), section 三 (Gated DeltaNet): recall S k from the state before the
-// gate, decay the state by g, write beta (v - recall) k^T.  The read-out uses
-//     o_t = S_t q_t = g_t (S_{t-1} q_t) + c_t (k_t . q_t),   c_t = beta_t (v_t - S_{t-1} k_t),
+// Both evaluate the gated delta-rule equation of "Qwen3.8-27B 架构深读"
+// (feifeigd.github.io, 2026-08-17), section 三 (Gated DeltaNet),
+// S_t = g_t S_{t-1} + c_t k_t^T with c_t = beta_t (v_t - S_{t-1} k_t), whose error
+// term reads the state before the gate.  The read-out uses
+//     o_t = S_t q_t = g_t (S_{t-1} q_t) + c_t (k_t . q_t),
 // so one read of each state row yields everything: two dot products (with k and
 // with q) and the rank-one update.
 //

@@ -11,6 +11,7 @@ Names mirror include/gdn.h:
     decode_step_slots(q, k, v, g, beta, pool, slots) -> o   (slot b of the pool per row)
     state_init(state, init=None), state_reset(state, slots=None)
     preprocess(xq, xk, xv, conv_w, a_logit, b_logit, ...) -> (q, k, v, g, beta, conv_state)
+    layer_prefill(xq, xk, xv, conv_w, a_logit, b_logit, ...) -> (o, final_state, conv_state, q, k, v)
     prefill_set_marks([ev0, ev1, ev2])                 (profiling hook)
     state_bytes(...), prefill_workspace_bytes(...), prefill_algorithm(...)
 """
@@ -47,6 +48,8 @@ SIGNATURES = {
                                      _i32, _i32, _vp]),
     "gdn_prefill_noalloc": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32,
                                    _vp, _vp, _vp, _i32, _i32, _vp]),
+    "gdn_layer_prefill": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                 _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _i32, _vp]),
     "gdn_prefill_set_marks": (_i32, [ctypes.POINTER(_vp), _i32]),
     "gdn_preprocess": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
                               _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -304,6 +307,58 @@ def preprocess(xq, xk, xv, conv_w, a_logit, b_logit, gate_bias=None, cu_seqlens=
         _dev_ptr(q, "q", xk.dtype), _dev_ptr(k, "k", xk.dtype), _dev_ptr(v, "v", xk.dtype),
         _dev_ptr(g, "g", torch.float32), _dev_ptr(beta, "beta", torch.float32), _stream(dev, stream)))
     return q, k, v, g, beta, conv_state_out
+
+
+def layer_prefill(xq, xk, xv, conv_w, a_logit, b_logit, gate_bias=None, cu_seqlens=None, conv_state_in=None,
+                  conv_state_out=None, activation=GDN_ACT_NONE, initial_state=None, chunk=CHUNK_AUTO,
+                  cu_seqlens_device=None, out=None, final_state=None, qkv=None, gates=None, workspace=None,
+                  stream=None, variant=GDN_VARIANT_GATED_DELTA):
+    """gdn_layer_prefill: the pre-processing and the chunked prefill in one
+    call from the raw projections (bf16, d = 128).
+
+    Arguments as for preprocess() and prefill(); qkv: optional (q, k, v)
+    output buffers for the processed inputs; gates: optional (g, beta) outputs
+    (not formed when None).  Returns (o, final_state, conv_state_out, q, k, v).
+    """
+    import torch
+    N, H, d = xk.shape
+    dev = xk.device
+    if isinstance(activation, str):
+        activation = {"none": GDN_ACT_NONE, "silu": GDN_ACT_SILU}[activation]
+    n_seq, cu_host, cu_dev = _cu_pair(cu_seqlens, cu_seqlens_device, dev)
+    code = _dtype_code(xk)
+    for name, t in (("xq", xq), ("xv", xv)):
+        if t.dtype != xk.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from xk dtype {xk.dtype}")
+    if out is None:
+        out = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+    if final_state is None:
+        final_state = torch.empty((n_seq, H, d, d), dtype=torch.float32, device=dev)
+    if conv_state_out is None:
+        conv_state_out = torch.empty((n_seq, 3, 3, H, d), dtype=xk.dtype, device=dev)
+    if qkv is None:
+        qkv = (torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv))
+    q, k, v = qkv
+    g, beta = (None, None) if gates is None else gates
+    ws_bytes = prefill_workspace_bytes(N, n_seq, H, d, d, code, chunk)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_ptr = _dev_ptr(workspace, "workspace") if ws_bytes else None
+    ws_len = workspace.numel() * workspace.element_size() if (ws_bytes and workspace is not None) else 0
+    cu_host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    _check(lib().gdn_layer_prefill(
+        _dev_ptr(xq, "xq"), _dev_ptr(xk, "xk"), _dev_ptr(xv, "xv"), code,
+        _dev_ptr(conv_w, "conv_w", torch.float32), _dev_ptr(conv_state_in, "conv_state_in", xk.dtype),
+        _dev_ptr(conv_state_out, "conv_state_out", xk.dtype), activation,
+        _dev_ptr(a_logit, "a_logit", torch.float32), _dev_ptr(b_logit, "b_logit", torch.float32),
+        _dev_ptr(gate_bias, "gate_bias", torch.float32),
+        _dev_ptr(cu_dev, "cu_seqlens_device", torch.int32), cu_host_ptr, n_seq, N, H, d,
+        _dev_ptr(initial_state, "initial_state", torch.float32), _dev_ptr(out, "out", torch.float32),
+        _dev_ptr(final_state, "final_state", torch.float32),
+        _dev_ptr(q, "q", xk.dtype), _dev_ptr(k, "k", xk.dtype), _dev_ptr(v, "v", xk.dtype),
+        _dev_ptr(g, "g", torch.float32), _dev_ptr(beta, "beta", torch.float32),
+        chunk, ws_ptr, ws_len, variant, _stream(dev, stream)))
+    return out, final_state, conv_state_out, q, k, v
 
 
 def decode_step_slots(q, k, v, g, beta, state_pool, slots, slots_host="auto", out=None, stream=None,

@@ -344,3 +344,18 @@ def test_noalloc_refuses_sizes_beyond_its_scratch():
                                None, FAKE * 4096, FAKE * 8192, gdn.CHUNK_64, 0, None)
     assert gdn.STATUS[st] == "GDN_ERR_WORKSPACE"
     assert b"scratch" in L.gdn_last_error()
+
+
+def test_layer_prefill_refuses_what_it_does_not_build():
+    """The fused layer runs the chunked bf16 path with d = 128 only; other
+    dtypes and head sizes are refused before any device call."""
+    L = gdn.lib()
+    cu = (ctypes.c_int32 * 2)(0, 64)
+    args = lambda dtype, d, chunk: (FAKE, FAKE, FAKE, dtype, FAKE, None, FAKE * 2, gdn.GDN_ACT_SILU, FAKE, FAKE,
+                                    None, FAKE * 3, cu, 1, 64, 4, d, None, FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7,
+                                    FAKE * 8, None, None, chunk, None, 0, 0, None)
+    for dtype, d, chunk in ((gdn.GDN_FP32, 128, gdn.CHUNK_AUTO), (gdn.GDN_BF16, 64, gdn.CHUNK_AUTO),
+                            (gdn.GDN_BF16, 128, gdn.CHUNK_SERIAL)):
+        st = L.gdn_layer_prefill(*args(dtype, d, chunk))
+        assert gdn.STATUS[st] == "GDN_ERR_UNSUPPORTED", (dtype, d, chunk, gdn.STATUS[st])
+        assert b"gdn_preprocess" in L.gdn_last_error()

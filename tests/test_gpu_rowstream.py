@@ -7,7 +7,7 @@ import torch
 from gpu_helpers import DEV, gpu_prefill, oracle_prefill, say
 from linear_attention_recurrence_gated_amd import gdn
 from linear_attention_recurrence_gated_amd import workloads as w
-from parity import TOL_BF16, rel_max_err, tol_for
+from parity import TOL_BF16, TOL_FP32, rel_max_err, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -124,3 +124,16 @@ def test_state_init_and_reset():
     gdn.state_init(st)
     torch.cuda.synchronize()
     assert torch.count_nonzero(st).item() == 0
+
+
+def test_fp32_prefill_d128_long(oracle_lib):
+    """fp32 q/k/v at d = 128 over 4096 tokens (the token-serial kernel), slow
+    decay and a nonzero initial state, against the oracle at the fp32 bar."""
+    say("fp32 prefill d=128 T=4096 H=4")
+    inp = w.make_prefill([4096], H=4, d=128, dtype="fp32", seed=61, gate_shift=-3.0, init_std=0.1, packed=False)
+    assert gdn.prefill_algorithm(gdn.GDN_FP32, 128, 128) == gdn.CHUNK_SERIAL
+    o, s = gpu_prefill(inp)
+    o_ref, s_ref = oracle_prefill(inp)
+    eo, es = rel_max_err(o, o_ref), rel_max_err(s, s_ref)
+    say(f"fp32 d=128 T=4096 errors o={eo:.2e} state={es:.2e}")
+    assert eo <= TOL_FP32 and es <= TOL_FP32
