@@ -227,19 +227,26 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 
 // Locate global chunk gc: first token t0 and length n (1..64).
 __device__ __forceinline__ void locate_chunk(int64_t gc, const int32_t *cu, const int32_t *chunk_base, int n_seq,
-                                             int64_t total_tokens, int64_t &t0, int &n) {
+                                             int64_t total_tokens, int64_t &t0, int &n, int &seq) {
     if (cu) {
         int lo = 0, hi = n_seq;  // largest s with chunk_base[s] <= gc (sequences of length 0 never match)
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (chunk_base[mid] <= gc) lo = mid; else hi = mid;
         }
+        seq = lo;
         t0 = (int64_t)cu[lo] + (gc - chunk_base[lo]) * C;
         n = (int)min((int64_t)C, (int64_t)cu[lo + 1] - t0);
     } else {
+        seq = 0;
         t0 = gc * C;
         n = (int)min((int64_t)C, total_tokens - t0);
     }
+}
+__device__ __forceinline__ void locate_chunk(int64_t gc, const int32_t *cu, const int32_t *chunk_base, int n_seq,
+                                             int64_t total_tokens, int64_t &t0, int &n) {
+    int seq;
+    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, t0, n, seq);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -723,14 +730,40 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
 // (llmdeepdive.com), section Conceito (a convolution of kernel 4 beside the
 // gated state) and the per-token gate and strength of "Qwen3.8-27B 架构深读",
 // section 三, formed here with the per-row arithmetic of gdn_preprocess (the
-// same bits): for each of q, k, v a thread owns 8 channels of 4 consecutive
-// rows (16 lanes per row), loads the 7 raw rows of its window once (the 3 rows
-// before a sequence's first token come from its conv state, or are zero),
-// and writes the processed rows to the caller's q, k, v and, for q and k, to
-// the row tiles; wave 0 maps the gates.  The rest is the chunk preparation.
-// Rows past the chunk's end are formed from clamped windows: any finite
-// values do there (see the header of this file), and they are not stored.
-// The returned conv state is written afterwards by k_conv_state.
+// same bits).  Every load is issued up front: the raw v window rows and taps
+// into registers, the raw q and k rows of the chunk straight into the two row
+// tiles (direct global->LDS copies, rows past the end repeating the last
+// one), the three rows in front of the chunk (its sequence's earlier tokens,
+// else its conv state, else zeros) into the scratch area, and the logits
+// (wave 0).  A thread owns 8 channels of 4 consecutive rows (16 lanes per
+// row).  v is formed first, from registers, while the copies land; then q
+// and k: each thread reads its 7-row window from LDS, and after a barrier
+// writes its 4 processed rows over the raw ones in the tile, where the chunk
+// preparation reads them.  Processed rows go to the caller's q, k, v as well
+// (the state chain reads them).  Rows past the chunk's end are formed from
+// repeated rows: any finite values do there (see the header of this file),
+// and they are not stored.  The returned conv state is written afterwards by
+// k_conv_state.
+__device__ __forceinline__ void layer_rows(const float (&tap)[8][4], const uint4 (&wr)[7], int act, bool normalise,
+                                           int i4, int n, uint16_t *__restrict__ y, int64_t rs, char *tile) {
+    using V = Vec8<uint16_t>;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = 4 * i4 + j;
+        float w0[8], w1[8], w2[8], cur[8], acc[8];
+        V::unpack(wr[j], w0);
+        V::unpack(wr[j + 1], w1);
+        V::unpack(wr[j + 2], w2);
+        V::unpack(wr[j + 3], cur);
+        pre_row<16>(tap, w0, w1, w2, cur, act, normalise, acc);
+        const uint32_t p0 = pack_bf16x2(acc[0], acc[1]), p1 = pack_bf16x2(acc[2], acc[3]),
+                       p2 = pack_bf16x2(acc[4], acc[5]), p3 = pack_bf16x2(acc[6], acc[7]);
+        if (t < n) store_nt16(y + t * rs, p0, p1, p2, p3);
+        if (tile) *reinterpret_cast<u32x4_t *>(tile + t * 256 + (((threadIdx.x & 15) ^ (t & 15)) << 4)) =
+            u32x4_t{p0, p1, p2, p3};
+    }
+}
+
 __global__ __launch_bounds__(256, 4) void k_layer_prep(LayerRaw raw, const int32_t *__restrict__ cu,
                                                     const int32_t *__restrict__ chunk_base, int n_seq,
                                                     int64_t total_tokens, int H, int erase, int has_g,
@@ -745,21 +778,62 @@ __global__ __launch_bounds__(256, 4) void k_layer_prep(LayerRaw raw, const int32
     const int64_t gc = blockIdx.x / H;
     const int h = blockIdx.x % H;
     int64_t t0;
-    int n;
-    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, t0, n);
+    int n, sq;
+    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, t0, n, sq);
+    const int64_t q0 = cu ? cu[sq] : 0;  // the sequence's first token
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
     char *rec = recs + (gc * H + h) * (int64_t)REC_BYTES;
     const int64_t rs = (int64_t)H * DK;
+    const int64_t col = (int64_t)h * DK;
+    const int i4 = tid >> 4, lr = tid & 15;  // rows 4 i4 .. 4 i4 + 3, channels 8 lr .. 8 lr + 7
+    using V = Vec8<uint16_t>;
 
     __shared__ PrepSmem S;
+    char *front = reinterpret_cast<char *>(S.scr);  // the 3 rows in front of the chunk: [q, k][3][256 B]
 
-    // the gates (wave 0): loads first, so that they overlap the row work
-    float gl = 1.f, bl = 0.f;
+    // raw input at chunk row m (-3 <= m), clamped to the chunk's last row;
+    // before the sequence's first token: its conv state, or NULL for zeros
+    auto src = [&](const uint16_t *x, int tau, int m) -> const uint16_t * {
+        const int64_t p = t0 + min(m, n - 1);
+        if (p >= q0) return x + p * rs + col;
+        if (raw.st_in) return raw.st_in + ((int64_t)(sq * 3 + tau) * 3 + (3 - (q0 - p))) * rs + col;
+        return nullptr;
+    };
+
+    // v: taps and window rows 4 i4 - 3 .. 4 i4 + 3
+    float tap[8][4];
+    load_taps(raw.w + ((int64_t)(2 * H + h) * DK + 8 * lr) * 4, tap);
+    uint4 wr[7];
+#pragma unroll
+    for (int m = 0; m < 7; ++m) {
+        const uint16_t *p = src(raw.xv, 2, 4 * i4 - 3 + m);
+        wr[m] = p ? V::load(p + 8 * lr) : V::zero();
+    }
+    // q, k rows of the chunk -> the row tiles
+    dma_rows(S.QT, raw.xq + t0 * rs + col, rs, n, lane, wave, 4);
+    dma_rows(S.KL, raw.xk + t0 * rs + col, rs, n, lane, wave, 4);
+    // the rows in front of the chunk (threads 0 .. 95: tensor, row, 16-byte unit)
+    uint4 fr = V::zero();
+    if (tid < 96) {
+        const int tau = tid / 48, j = (tid % 48) >> 4;
+        const uint16_t *p = src(tau ? raw.xk : raw.xq, tau, j - 3);
+        if (p) fr = V::load(p + 8 * lr);
+    }
+    // the gate logits (wave 0)
+    float a = 0.f, b = 0.f, bias = 0.f;
     if (wave == 0) {
         const int64_t off = (t0 + min(lane, n - 1)) * H + h;
-        const float a = has_g ? raw.a_logit[off] : 0.f, b = raw.b_logit[off];
-        const float bias = raw.bias ? raw.bias[h] : 0.f;
+        a = has_g ? raw.a_logit[off] : 0.f;
+        b = raw.b_logit[off];
+        bias = raw.bias ? raw.bias[h] : 0.f;
+    }
+
+    layer_rows(tap, wr, raw.act, false, i4, n, raw.v + t0 * rs + col + 8 * lr, rs, nullptr);
+
+    // the gates (wave 0)
+    float gl = 1.f, bl = 0.f;
+    if (wave == 0) {
         gl = gate_g(a, bias);
         bl = gate_beta(b);
         if (lane < n) {
@@ -767,64 +841,22 @@ __global__ __launch_bounds__(256, 4) void k_layer_prep(LayerRaw raw, const int32
             if (raw.beta) raw.beta[(t0 + lane) * H + h] = bl;
         }
     }
+    if (tid < 96) *reinterpret_cast<uint4 *>(front + tid * 16) = fr;
+    wait_all_vmem();
+    lds_barrier();  // raw q, k rows and the front rows in LDS
 
-    // the sequence holding this chunk and the first token of that sequence
-    int sq = 0;
-    int64_t q0 = 0;
-    if (cu) {
-        int lo = 0, hi = n_seq;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (chunk_base[mid] <= gc) lo = mid; else hi = mid;
-        }
-        sq = lo;
-        q0 = cu[lo];
-    }
-    const int i4 = tid >> 4, lr = tid & 15;  // rows 4 i4 .. 4 i4 + 3, channels 8 lr .. 8 lr + 7
-    using V = Vec8<uint16_t>;
 #pragma unroll 1
-    for (int tau = 0; tau < 3; ++tau) {
-        const uint16_t *x = (tau == 0 ? raw.xq : tau == 1 ? raw.xk : raw.xv) + (int64_t)h * DK + 8 * lr;
-        float tap[8][4];
-        {
-            const float *wp = raw.w + ((int64_t)(tau * H + h) * DK + 8 * lr) * 4;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float4 f = *reinterpret_cast<const float4 *>(wp + 4 * e);
-                tap[e][0] = f.x; tap[e][1] = f.y; tap[e][2] = f.z; tap[e][3] = f.w;
-            }
-        }
-        // window rows 4 i4 - 3 + m, m = 0..6, clamped to the chunk's last row;
-        // before the sequence's first token: its conv state, or zero
-        typename V::raw_t wr[7];
+    for (int tau = 0; tau < 2; ++tau) {
+        char *tile = tau ? S.KL : S.QT;
+        load_taps(raw.w + ((int64_t)(tau * H + h) * DK + 8 * lr) * 4, tap);
 #pragma unroll
         for (int m = 0; m < 7; ++m) {
-            const int64_t p = t0 + min(4 * i4 - 3 + m, n - 1);
-            if (p >= q0) {
-                wr[m] = V::load(x + p * rs);
-            } else if (raw.st_in) {
-                wr[m] = V::load(raw.st_in + ((int64_t)(sq * 3 + tau) * 3 + (3 - (q0 - p))) * rs +
-                                (int64_t)h * DK + 8 * lr);
-            } else {
-                wr[m] = V::zero();
-            }
+            const int row = 4 * i4 - 3 + m;
+            wr[m] = row >= 0 ? *reinterpret_cast<const uint4 *>(tile + row * 256 + ((lr ^ (row & 15)) << 4))
+                             : *reinterpret_cast<const uint4 *>(front + (tau * 3 + row + 3) * 256 + lr * 16);
         }
-        uint16_t *y = (tau == 0 ? raw.q : tau == 1 ? raw.k : raw.v) + (int64_t)h * DK + 8 * lr;
-        char *tile = tau == 0 ? S.QT : S.KL;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = 4 * i4 + j;
-            float w0[8], w1[8], w2[8], cur[8], acc[8];  // the window, unpacked per row
-            V::unpack(wr[j], w0);
-            V::unpack(wr[j + 1], w1);
-            V::unpack(wr[j + 2], w2);
-            V::unpack(wr[j + 3], cur);
-            pre_row<16>(tap, w0, w1, w2, cur, raw.act, tau < 2, acc);
-            const uint32_t p0 = pack_bf16x2(acc[0], acc[1]), p1 = pack_bf16x2(acc[2], acc[3]),
-                           p2 = pack_bf16x2(acc[4], acc[5]), p3 = pack_bf16x2(acc[6], acc[7]);
-            if (t < n) store_nt16(y + (t0 + t) * rs, p0, p1, p2, p3);
-            if (tau < 2) *reinterpret_cast<u32x4_t *>(tile + t * 256 + ((lr ^ (t & 15)) << 4)) = u32x4_t{p0, p1, p2, p3};
-        }
+        lds_barrier();  // every raw row read before any is overwritten
+        layer_rows(tap, wr, raw.act, true, i4, n, (tau ? raw.k : raw.q) + t0 * rs + col + 8 * lr, rs, tile);
     }
     prep_body(S, rec, n, gl, bl, has_g != 0, erase, wave, lane, g4, r);
 }

@@ -60,6 +60,15 @@ template <> struct Vec8<float> {
 __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 __device__ __forceinline__ float softplusf_(float x) { return x > 0.f ? x + log1pf(__expf(-x)) : log1pf(__expf(x)); }
 
+// The 32 taps of one lane: 8 channels x 4 taps, oldest input first.
+__device__ __forceinline__ void load_taps(const float *__restrict__ wp, float (&tap)[8][4]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float4 t = *reinterpret_cast<const float4 *>(wp + 4 * e);
+        tap[e][0] = t.x; tap[e][1] = t.y; tap[e][2] = t.z; tap[e][3] = t.w;
+    }
+}
+
 // One token of one (tensor, head) row slice: convolution over the window
 // w0..w2 (oldest first) and the current input, activation, norm (over the
 // LPR lanes of the head), into acc.

@@ -89,14 +89,7 @@ __global__ __launch_bounds__(256) void k_preprocess(const TIn *__restrict__ xq, 
     const bool normalise = tau < 2;
 
     float tap[8][4];
-    {
-        const float *wp = w + ((int64_t)(tau * H + hc) * D + 8 * lr) * 4;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float4 f = *reinterpret_cast<const float4 *>(wp + 4 * e);
-            tap[e][0] = f.x; tap[e][1] = f.y; tap[e][2] = f.z; tap[e][3] = f.w;
-        }
-    }
+    load_taps(w + ((int64_t)(tau * H + hc) * D + 8 * lr) * 4, tap);
     const int s0 = cu ? seq_of(cu, n_seq, ta) : 0;
     const int64_t t0 = cu ? cu[s0] : 0, t1 = cu ? cu[s0 + 1] : total_tokens;
 
