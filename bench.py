@@ -63,6 +63,7 @@ LAYER_QKV_ROUND_TRIP_PER_TOKEN_HEAD = 2 * 3 * D * 2                             
 KERNEL_SOURCES = {
     "k_chunk_prep": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h", "gdn_conv.h"),
     "k_chunk_chain": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h", "gdn_conv.h"),
+    "k_layer_prep": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h", "gdn_conv.h"),
     "k_decode_step": ("gdn_rowstream.hip", "gdn_device.h"),
     "k_preprocess": ("gdn_preprocess.hip", "gdn_device.h", "gdn_conv.h"),
 }
@@ -398,6 +399,7 @@ def layer_entry(layer_ms, two_ms, kern):
     nbytes = LAYER_BYTES_PER_TOKEN_HEAD * T * H + PRE_BYTES_FIXED + STATE_BYTES_PER_HEAD * H
     design = nbytes + LAYER_QKV_ROUND_TRIP_PER_TOKEN_HEAD * T * H
     gbs = nbytes / (layer_ms / 1e3) / 1e9
+    tl, tc = load_traffic("k_layer_prep"), load_traffic("k_chunk_chain")
     return {"workload": "gdn_layer_prefill: raw projections -> conv (4 taps) + SiLU + L2 norm + gate maps + "
                         "chunked prefill, T = 4096, H = 48, d = 128, bf16, conv state in/out, zero initial state",
             "mean_ms": layer_ms, "tokens_per_s_layer": T / (layer_ms / 1e3),
@@ -405,7 +407,8 @@ def layer_entry(layer_ms, two_ms, kern):
             "kernels_ms": kern,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
-                         "bytes_with_qkv_round_trip": design}}
+                         "bytes_with_qkv_round_trip": design,
+                         "traffic": None if tl is None or tc is None else tl + tc}}
 
 
 def bench_config4(torch, gdn, w, runs):
