@@ -410,6 +410,7 @@ gdn_status gdn_layer_prefill(const void *xq, const void *xk, const void *xv, gdn
     raw.v = static_cast<uint16_t *>(v);
     raw.g = g;
     raw.beta = beta;
+    raw.state_here = 0;  // the launch decides
     return hip_status(gdn::launch_prefill_chunked(q, k, v, nullptr, nullptr, cu_seqlens, cu_seqlens_host, n_seq,
                                                   total_tokens, H, initial_state, o, final_state, workspace,
                                                   erase_of(variant), chunked_mode(algo), marks.ev,

@@ -742,8 +742,11 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
 // preparation reads them.  Processed rows go to the caller's q, k, v as well
 // (the state chain reads them).  Rows past the chunk's end are formed from
 // repeated rows: any finite values do there (see the header of this file),
-// and they are not stored.  The returned conv state is written afterwards by
-// k_conv_state.
+// and they are not stored.  The returned conv state (the last three raw
+// inputs of each sequence) is written by the workgroup of the sequence's last
+// chunk, after every read of the starting state in that workgroup, when no
+// other workgroup reads that starting state later (see layer_state_here);
+// otherwise by k_conv_state afterwards.
 __device__ __forceinline__ void layer_rows(const float (&tap)[8][4], const uint4 (&wr)[7], int act, bool normalise,
                                            int i4, int n, uint16_t *__restrict__ y, int64_t rs, char *tile) {
     using V = Vec8<uint16_t>;
@@ -857,6 +860,23 @@ __global__ __launch_bounds__(256, 4) void k_layer_prep(LayerRaw raw, const int32
         }
         lds_barrier();  // every raw row read before any is overwritten
         layer_rows(tap, wr, raw.act, true, i4, n, (tau ? raw.k : raw.q) + t0 * rs + col + 8 * lr, rs, tile);
+    }
+    // the returned conv state, from the sequence's last chunk (threads 0 .. 47:
+    // tensor, 16-byte unit; the three slots in one thread).  This workgroup's
+    // other reads of the starting state were consumed above; in place, slot
+    // j is read (for slot j - 1 of a sequence shorter than three) before it
+    // is written, in this thread's own order.
+    if (raw.state_here && tid < 48 && t0 + n == (cu ? (int64_t)cu[sq + 1] : total_tokens)) {
+        const int tau = tid >> 4;
+        uint4 x[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const uint16_t *p = src(tau == 0 ? raw.xq : tau == 1 ? raw.xk : raw.xv, tau, n - 3 + j);
+            x[j] = p ? V::load(p + 8 * lr) : V::zero();
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            *reinterpret_cast<uint4 *>(raw.st_out + ((int64_t)(sq * 3 + tau) * 3 + j) * rs + col + 8 * lr) = x[j];
     }
     prep_body(S, rec, n, gl, bl, has_g != 0, erase, wave, lane, g4, r);
 }
@@ -1623,6 +1643,18 @@ __global__ __launch_bounds__(512) void k_scan_combine(int n_seq, int H, const in
 // and copies per pair, is faster (measured on packed batches of 8 sequences
 // of 1,224 to 54,318 tokens: 24 heads favour the column split, 48 heads the
 // two-workgroup form).
+// Whether k_layer_prep can return the conv state itself: every sequence has
+// a chunk (none is empty), and, when the state is updated in place, no
+// sequence spans two chunks (its one workgroup reads the starting state
+// before it writes the returned one; across workgroups nothing orders them).
+bool layer_state_here(const int32_t *cu_host, int64_t n_seq, int64_t N, bool in_place) {
+    for (int64_t s = 0; s < n_seq; ++s) {
+        const int64_t len = cu_host ? (int64_t)cu_host[s + 1] - cu_host[s] : N;
+        if (len == 0 || (in_place && len > C)) return false;
+    }
+    return n_seq > 0;
+}
+
 bool use_column_split(int64_t sum_chunks, int64_t max_chunks, int64_t n_long, int H) {
     return CS_TILES * (int64_t)H * n_long <= 256 && 10 * CS_TILES * (int64_t)H * sum_chunks <= 11 * 256 * max_chunks;
 }
@@ -1691,9 +1723,14 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
         std::copy(sp.base, sp.base + sp.P + 1, segs.h_base);
         std::copy(sp.seg0, sp.seg0 + n_seq + 1, segs.h_seg0);
     }
+    LayerRaw lr;
+    if (raw) {
+        lr = *raw;
+        lr.state_here = layer_state_here(cu_seqlens_host, n_seq, total_tokens, raw->st_in && raw->st_in == raw->st_out);
+    }
     if (n_chunks > 0) {
         if (raw)
-            hipLaunchKernelGGL(k_layer_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream, *raw, cu_seqlens,
+            hipLaunchKernelGGL(k_layer_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream, lr, cu_seqlens,
                                chunk_base, (int)n_seq, total_tokens, H, erase, raw->a_logit != nullptr ? 1 : 0, recs,
                                segs);
         else
@@ -1703,7 +1740,7 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (raw) {  // the returned conv state, after every chunk preparation has read the starting state
+    if (raw && !lr.state_here) {  // the returned conv state, after every chunk preparation has read the starting state
         e = launch_conv_state(true, DK, raw->xq, raw->xk, raw->xv, raw->st_in, raw->st_out, cu_seqlens, n_seq,
                               total_tokens, H, stream);
         if (e != hipSuccess) return e;

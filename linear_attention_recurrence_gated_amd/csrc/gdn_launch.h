@@ -52,6 +52,7 @@ struct LayerRaw {
     int act;                          // 0 none, 1 SiLU
     uint16_t *q, *k, *v;              // [N][H][128] outputs
     float *g, *beta;                  // [N][H] outputs, or NULL
+    int state_here;                   // set by the launch: k_layer_prep returns the conv state itself
 };
 
 // Chunkwise-parallel prefill (64-token chunks, d = 128, bf16 q/k/v).

@@ -100,11 +100,14 @@ def test_layer_equals_preprocess_then_prefill(name):
     assert_same(got, ref, ("o", "s", "st", "q", "k", "v", "g", "beta"), name)
 
 
-def test_layer_in_place_states_and_no_gate_outputs():
+@pytest.mark.parametrize("lengths", [[130, 0, 64, 1, 333], [1, 2, 3, 64, 17, 2]])
+def test_layer_in_place_states_and_no_gate_outputs(lengths):
     """conv_state_out == conv_state_in and final_state == initial_state; g and
-    beta not requested."""
-    say("layer in place")
-    inp = w.make_preprocess([130, 0, 64, 1, 333], H=3, d=128, dtype="bf16", seed=21, activation="silu")
+    beta not requested.  With an empty or a multi-chunk sequence the returned
+    conv state is written after the chunk preparation (k_conv_state); with
+    single-chunk sequences only, by the chunk preparation itself."""
+    say("layer in place", lengths)
+    inp = w.make_preprocess(lengths, H=3, d=128, dtype="bf16", seed=21, activation="silu")
     d = dev_inputs(inp)
     s0 = torch.from_numpy(initial_states(inp, 3, 6)).to(DEV)
     ref = two_calls(d, inp, s0, gdn.CHUNK_64)
