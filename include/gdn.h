@@ -82,6 +82,10 @@ enum {
                                  (the chunk-parallel state accumulation of "Qwen3.8-27B 架构深读",
                                  section 三); picked by GDN_CHUNK_64 for few (sequence, head) pairs
                                  when it is expected to be faster */
+#define GDN_CHUNK_16 16       /* chunked with 16- or 32-token chunks: the same kernels with each     */
+#define GDN_CHUNK_32 32       /* chunk's 64-row tiles part filled, one chain per (sequence, head).
+                                 The chunk length changes no result beyond rounding; these exist to
+                                 test that (more chunks, more records: slower than GDN_CHUNK_64) */
 
 /* Variants of the recurrence (the `variant` argument of gdn_prefill,
  * gdn_decode_step and gdn_decode_step_slots), from the equations of the
@@ -106,7 +110,8 @@ size_t gdn_state_bytes(int64_t n_seq, int32_t H, int32_t dk, int32_t dv);
 
 /* Which algorithm gdn_prefill would run for these arguments:
  * GDN_CHUNK_SERIAL, GDN_CHUNK_64 (or the explicit GDN_CHUNK_64_CHAIN /
- * GDN_CHUNK_64_SCAN asked for), or 0 if the combination is not supported. */
+ * GDN_CHUNK_64_SCAN / GDN_CHUNK_32 / GDN_CHUNK_16 asked for), or 0 if the
+ * combination is not supported. */
 int32_t gdn_prefill_algorithm(gdn_dtype dtype, int32_t dk, int32_t dv, int32_t chunk);
 
 /* Set a state before any token arrives ("attention and memory", stethem.com,
@@ -143,8 +148,9 @@ size_t gdn_prefill_workspace_bytes(int64_t total_tokens, int64_t n_seq, int32_t 
  *                             not otherwise overlap it.
  *   o             [N][H][dv]  fp32 output (must not overlap any input)
  *   final_state   [n_seq][H][dv][dk] fp32 output
- *   chunk         GDN_CHUNK_AUTO, GDN_CHUNK_SERIAL, GDN_CHUNK_64, GDN_CHUNK_64_CHAIN or
- *                 GDN_CHUNK_64_SCAN (1 to 64 sequences and at least one token, else GDN_ERR_UNSUPPORTED)
+ *   chunk         GDN_CHUNK_AUTO, GDN_CHUNK_SERIAL, GDN_CHUNK_64, GDN_CHUNK_64_CHAIN,
+ *                 GDN_CHUNK_64_SCAN (1 to 64 sequences and at least one token, else GDN_ERR_UNSUPPORTED),
+ *                 GDN_CHUNK_32 or GDN_CHUNK_16
  *   workspace     device scratch of at least gdn_prefill_workspace_bytes();
  *                 may be NULL when that is 0.  Its contents on entry do not matter.
  *   variant       GDN_VARIANT_* flags (0: the gated delta rule)
@@ -280,8 +286,8 @@ gdn_status gdn_preprocess(const void *xq, const void *xk, const void *xv, gdn_dt
  *                          a_logit ignored, and may be NULL, with GDN_VARIANT_NO_GATE)
  *   cu_seqlens, cu_seqlens_host, n_seq, total_tokens, H, initial_state, o,
  *   final_state, chunk, workspace, workspace_bytes, variant
- *                          as for gdn_prefill (chunk: GDN_CHUNK_AUTO or one of
- *                          the GDN_CHUNK_64 forms; the workspace size is
+ *                          as for gdn_prefill (chunk: GDN_CHUNK_AUTO, one of the
+ *                          GDN_CHUNK_64 forms, GDN_CHUNK_32 or GDN_CHUNK_16; the workspace size is
  *                          gdn_prefill_workspace_bytes(..., GDN_BF16, chunk))
  *   q, k, v    [N][H][d] bf16 outputs: the processed inputs of the recurrence
  *              (caller-owned; the state chain reads them)

@@ -59,12 +59,19 @@ size_t elem_bytes(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
 
 int erase_of(int32_t variant) { return (variant & GDN_VARIANT_NO_ERASE) ? 0 : 1; }
 
-bool is_chunked(int32_t algo) { return algo == GDN_CHUNK_64 || algo == GDN_CHUNK_64_CHAIN || algo == GDN_CHUNK_64_SCAN; }
+bool is_chunked(int32_t algo) {
+    return algo == GDN_CHUNK_64 || algo == GDN_CHUNK_64_CHAIN || algo == GDN_CHUNK_64_SCAN || algo == GDN_CHUNK_16 ||
+           algo == GDN_CHUNK_32;
+}
 
+// The shorter chunks run the one-chain forms (the library picks between them).
 int chunked_mode(int32_t algo) {
     return algo == GDN_CHUNK_64_CHAIN ? gdn::CHUNKED_CHAIN : algo == GDN_CHUNK_64_SCAN ? gdn::CHUNKED_SCAN
-                                                                                     : gdn::CHUNKED_AUTO;
+           : (algo == GDN_CHUNK_16 || algo == GDN_CHUNK_32) ? gdn::CHUNKED_CHAIN
+                                                            : gdn::CHUNKED_AUTO;
 }
+
+int chunk_len_of(int32_t algo) { return algo == GDN_CHUNK_16 ? 16 : algo == GDN_CHUNK_32 ? 32 : 64; }
 
 struct Range {
     const void *p;
@@ -88,6 +95,8 @@ int32_t pick_algorithm(gdn_dtype dtype, int32_t dk, int32_t dv, int32_t chunk) {
         case GDN_CHUNK_64: return chunked_built ? GDN_CHUNK_64 : 0;
         case GDN_CHUNK_64_CHAIN: return chunked_built ? GDN_CHUNK_64_CHAIN : 0;
         case GDN_CHUNK_64_SCAN: return chunked_built ? GDN_CHUNK_64_SCAN : 0;
+        case GDN_CHUNK_16: return chunked_built ? GDN_CHUNK_16 : 0;
+        case GDN_CHUNK_32: return chunked_built ? GDN_CHUNK_32 : 0;
         default: return 0;
     }
 }
@@ -211,7 +220,7 @@ size_t gdn_prefill_workspace_bytes(int64_t total_tokens, int64_t n_seq, int32_t 
     if (total_tokens < 0 || n_seq < 0 || H <= 0) return 0;
     const int32_t algo = pick_algorithm(dtype, dk, dv, chunk);
     if (!is_chunked(algo)) return 0;
-    return gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H, chunked_mode(algo));
+    return gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H, chunked_mode(algo), chunk_len_of(algo));
 }
 
 gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dtype, const float *g,
@@ -230,7 +239,7 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
     if (!algo)
         return fail(GDN_ERR_UNSUPPORTED, "prefill: dtype=%d dk=%d dv=%d chunk=%d not supported", (int)dtype, dk, dv,
                     chunk);
-    if (is_chunked(algo) ? !gdn::prefill_chunked_fits(total_tokens, n_seq, H) : !gdn::prefill_serial_fits(dk, n_seq, H))
+    if (is_chunked(algo) ? !gdn::prefill_chunked_fits(total_tokens, n_seq, H, chunk_len_of(algo)) : !gdn::prefill_serial_fits(dk, n_seq, H))
         return fail(GDN_ERR_SHAPE, "prefill: n_seq=%lld total_tokens=%lld H=%d exceed one launch", (long long)n_seq,
                     (long long)total_tokens, H);
     // sequence offsets
@@ -281,7 +290,7 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
     if (algo == GDN_CHUNK_64_SCAN && !gdn::prefill_chunked_scan_supported(n_seq, total_tokens))
         return fail(GDN_ERR_UNSUPPORTED, "prefill: the chunk-level scan takes 1 to 64 sequences and at least one token");
     if (is_chunked(algo)) {
-        const size_t need = gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H, chunked_mode(algo));
+        const size_t need = gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H, chunked_mode(algo), chunk_len_of(algo));
         if (need > 0 && (!workspace || workspace_bytes < need))
             return fail(GDN_ERR_WORKSPACE, "prefill: workspace of %zu bytes needed, %zu given", need,
                         workspace ? workspace_bytes : (size_t)0);
@@ -290,7 +299,8 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
             if (overlap({workspace, need}, in)) return fail(GDN_ERR_ALIAS, "prefill: workspace overlaps an argument");
         return hip_status(gdn::launch_prefill_chunked(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, n_seq,
                                                       total_tokens, H, initial_state, o, final_state, workspace,
-                                                      erase_of(variant), chunked_mode(algo), marks.ev, st),
+                                                      erase_of(variant), chunked_mode(algo), marks.ev, st, nullptr,
+                                                      chunk_len_of(algo)),
                           "prefill (chunked) launch");
     }
     return hip_status(gdn::launch_prefill_serial(dtype == GDN_BF16, dk, q, k, v, g, beta, cu_seqlens, n_seq,
@@ -321,7 +331,7 @@ gdn_status gdn_layer_prefill(const void *xq, const void *xk, const void *xv, gdn
                     "layer_prefill: the fused layer runs the chunked algorithm on bf16 with d = 128 (dtype=%d d=%d "
                     "chunk=%d); use gdn_preprocess and gdn_prefill",
                     (int)dtype, d, chunk);
-    if (!gdn::prefill_chunked_fits(total_tokens, n_seq, H))
+    if (!gdn::prefill_chunked_fits(total_tokens, n_seq, H, chunk_len_of(algo)))
         return fail(GDN_ERR_SHAPE, "layer_prefill: n_seq=%lld total_tokens=%lld H=%d exceed one launch",
                     (long long)n_seq, (long long)total_tokens, H);
     if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr))
@@ -382,7 +392,7 @@ gdn_status gdn_layer_prefill(const void *xq, const void *xk, const void *xv, gdn
     if (algo == GDN_CHUNK_64_SCAN && !gdn::prefill_chunked_scan_supported(n_seq, total_tokens))
         return fail(GDN_ERR_UNSUPPORTED,
                     "layer_prefill: the chunk-level scan takes 1 to 64 sequences and at least one token");
-    const size_t need = gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H, chunked_mode(algo));
+    const size_t need = gdn::prefill_chunked_workspace_bytes(total_tokens, n_seq, H, chunked_mode(algo), chunk_len_of(algo));
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GDN_ERR_WORKSPACE, "layer_prefill: workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -414,7 +424,7 @@ gdn_status gdn_layer_prefill(const void *xq, const void *xk, const void *xv, gdn
     return hip_status(gdn::launch_prefill_chunked(q, k, v, nullptr, nullptr, cu_seqlens, cu_seqlens_host, n_seq,
                                                   total_tokens, H, initial_state, o, final_state, workspace,
                                                   erase_of(variant), chunked_mode(algo), marks.ev,
-                                                  (hipStream_t)stream, &raw),
+                                                  (hipStream_t)stream, &raw, chunk_len_of(algo)),
                       "layer_prefill launch");
 }
 

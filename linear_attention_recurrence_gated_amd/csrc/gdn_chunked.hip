@@ -194,13 +194,13 @@ struct WsLayout {
     size_t seg_cu_off, seg_base_off, seg0_off, r_off, m_off, sin_off;
 };
 
-WsLayout ws_layout(int64_t total_tokens, int64_t n_seq, int H, bool scan_area) {
+WsLayout ws_layout(int64_t total_tokens, int64_t n_seq, int H, bool scan_area, int cl) {
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     WsLayout L;
     L.base_off = 0;
     L.order_off = up((size_t)(n_seq + 1) * 4);
     L.rec_off = L.order_off + up((size_t)n_seq * 4);
-    const size_t max_chunks = (size_t)((total_tokens + C - 1) / C + n_seq);
+    const size_t max_chunks = (size_t)((total_tokens + cl - 1) / cl + n_seq);
     L.total = L.rec_off + max_chunks * (size_t)H * REC_BYTES;
     if (scan_area) {
         L.scan_cap = scan_capacity(n_seq, H);
@@ -227,7 +227,7 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 
 // Locate global chunk gc: first token t0 and length n (1..64).
 __device__ __forceinline__ void locate_chunk(int64_t gc, const int32_t *cu, const int32_t *chunk_base, int n_seq,
-                                             int64_t total_tokens, int64_t &t0, int &n, int &seq) {
+                                             int64_t total_tokens, int cl, int64_t &t0, int &n, int &seq) {
     if (cu) {
         int lo = 0, hi = n_seq;  // largest s with chunk_base[s] <= gc (sequences of length 0 never match)
         while (hi - lo > 1) {
@@ -235,18 +235,18 @@ __device__ __forceinline__ void locate_chunk(int64_t gc, const int32_t *cu, cons
             if (chunk_base[mid] <= gc) lo = mid; else hi = mid;
         }
         seq = lo;
-        t0 = (int64_t)cu[lo] + (gc - chunk_base[lo]) * C;
-        n = (int)min((int64_t)C, (int64_t)cu[lo + 1] - t0);
+        t0 = (int64_t)cu[lo] + (gc - chunk_base[lo]) * cl;
+        n = (int)min((int64_t)cl, (int64_t)cu[lo + 1] - t0);
     } else {
         seq = 0;
-        t0 = gc * C;
-        n = (int)min((int64_t)C, total_tokens - t0);
+        t0 = gc * cl;
+        n = (int)min((int64_t)cl, total_tokens - t0);
     }
 }
 __device__ __forceinline__ void locate_chunk(int64_t gc, const int32_t *cu, const int32_t *chunk_base, int n_seq,
-                                             int64_t total_tokens, int64_t &t0, int &n) {
+                                             int64_t total_tokens, int cl, int64_t &t0, int &n) {
     int seq;
-    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, t0, n, seq);
+    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, cl, t0, n, seq);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -272,15 +272,27 @@ __device__ __forceinline__ void lds_barrier() {
 // t * 256 + ((u ^ (t & 15)) << 4).
 
 // Copy 64 token rows (one chunk of one head, rows past n clamped to row n-1)
-// from global memory into a row tile, `step` and `nstep` spread the 16
-// one-kilobyte copies over the workgroup's waves.
-__device__ __forceinline__ void dma_rows(char *tile, const uint16_t *chunk, int64_t rs, int n, int lane, int step0,
-                                         int nstep) {
-    for (int a = step0; a < 16; a += nstep) {
-        const int t = 4 * a + (lane >> 4);
-        const int u = (lane & 15) ^ (t & 15);
-        const uint16_t *src = chunk + (int64_t)min(t, n - 1) * rs + 8 * u;
-        __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)(tile + a * FRAG), 16, 0, 0);
+// from global memory into a row tile, by a 4-wave workgroup: wave w copies
+// kilobytes w, w + 4, w + 8, w + 12 (rows 4a .. 4a + 3 of kilobyte a, one
+// row per 16 lanes).  A lane's rows are tl + 16 j, all with the same
+// (row & 15), so it copies the same 16-byte unit u of each; in a full chunk
+// its sources are one stride apart.
+__device__ __forceinline__ void dma_rows(char *tile, const uint16_t *chunk, int64_t rs, int n, int lane, int wave) {
+    const int tl = 4 * wave + (lane >> 4);
+    const int u = (lane & 15) ^ (tl & 15);
+    if (n == C) {
+        const uint16_t *src = chunk + (int64_t)tl * rs + 8 * u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(src + j * 16 * rs),
+                                             (lds_void *)(tile + (wave + 4 * j) * FRAG), 16, 0, 0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint16_t *src = chunk + (int64_t)min(tl + 16 * j, n - 1) * rs + 8 * u;
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
+                                             (lds_void *)(tile + (wave + 4 * j) * FRAG), 16, 0, 0);
+        }
     }
 }
 
@@ -368,7 +380,7 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int tid, int *wsum) {
     return r;
 }
 
-__global__ __launch_bounds__(PLAN_THREADS) void k_plan(const int32_t *__restrict__ cu, int n_seq,
+__global__ __launch_bounds__(PLAN_THREADS) void k_plan(const int32_t *__restrict__ cu, int n_seq, int cl,
                                                        int32_t *__restrict__ chunk_base,
                                                        int32_t *__restrict__ seq_order) {
     __shared__ int32_t bins[PLAN_BINS];
@@ -382,7 +394,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan(const int32_t *__restrict
     int carry = 0;
     for (int base = 0; base < n_seq; base += PLAN_THREADS) {
         const int s = base + tid;
-        const int cnt = s < n_seq ? (cu[s + 1] - cu[s] + C - 1) / C : 0;
+        const int cnt = s < n_seq ? (cu[s + 1] - cu[s] + cl - 1) / cl : 0;
         if (s < n_seq) atomicAdd(&bins[PLAN_BINS - 1 - min(cnt, PLAN_BINS - 1)], 1);
         const int inc = block_inclusive_scan(cnt, tid, wsum);
         if (s < n_seq) chunk_base[s] = carry + inc - cnt;
@@ -408,7 +420,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void k_plan(const int32_t *__restrict
     }
     __syncthreads();
     for (int s = tid; s < n_seq; s += PLAN_THREADS) {
-        const int cnt = (cu[s + 1] - cu[s] + C - 1) / C;
+        const int cnt = (cu[s + 1] - cu[s] + cl - 1) / cl;
         const int pos = atomicAdd(&bins[PLAN_BINS - 1 - min(cnt, PLAN_BINS - 1)], 1);
         seq_order[pos] = s;
     }
@@ -687,7 +699,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
                                                     const float *__restrict__ g, const float *__restrict__ beta,
                                                     const int32_t *__restrict__ cu,
                                                     const int32_t *__restrict__ chunk_base, int n_seq,
-                                                    int64_t total_tokens, int H, int erase,
+                                                    int64_t total_tokens, int H, int erase, int cl,
                                                     char *__restrict__ recs, ScanSegs segs) {
     if (blockIdx.x == 0 && segs.cu) {
         for (int i = threadIdx.x; i <= segs.P; i += 256) {
@@ -700,7 +712,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
     const int h = blockIdx.x % H;
     int64_t t0;
     int n;
-    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, t0, n);
+    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, cl, t0, n);
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
     char *rec = recs + (gc * H + h) * (int64_t)REC_BYTES;
@@ -717,8 +729,8 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const uint16_t *__restrict__
         bl = beta[off];
     }
     // q, k rows of the chunk -> LDS row tiles (8 one-kilobyte copies per wave)
-    dma_rows(S.KL, k + cbase, rs, n, lane, wave, 4);
-    dma_rows(S.QT, q + cbase, rs, n, lane, wave, 4);
+    dma_rows(S.KL, k + cbase, rs, n, lane, wave);
+    dma_rows(S.QT, q + cbase, rs, n, lane, wave);
     asm volatile("" : "+v"(gl), "+v"(bl));  // keeps the gate arithmetic after the copies are issued
     prep_body(S, rec, n, gl, bl, g != nullptr, erase, wave, lane, g4, r);
 }
@@ -769,7 +781,7 @@ __device__ __forceinline__ void layer_rows(const float (&tap)[8][4], const uint4
 
 __global__ __launch_bounds__(256, 4) void k_layer_prep(LayerRaw raw, const int32_t *__restrict__ cu,
                                                     const int32_t *__restrict__ chunk_base, int n_seq,
-                                                    int64_t total_tokens, int H, int erase, int has_g,
+                                                    int64_t total_tokens, int H, int erase, int has_g, int cl,
                                                     char *__restrict__ recs, ScanSegs segs) {
     if (blockIdx.x == 0 && segs.cu) {
         for (int i = threadIdx.x; i <= segs.P; i += 256) {
@@ -782,7 +794,7 @@ __global__ __launch_bounds__(256, 4) void k_layer_prep(LayerRaw raw, const int32
     const int h = blockIdx.x % H;
     int64_t t0;
     int n, sq;
-    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, t0, n, sq);
+    locate_chunk(gc, cu, chunk_base, n_seq, total_tokens, cl, t0, n, sq);
     const int64_t q0 = cu ? cu[sq] : 0;  // the sequence's first token
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
@@ -808,14 +820,20 @@ __global__ __launch_bounds__(256, 4) void k_layer_prep(LayerRaw raw, const int32
     float tap[8][4];
     load_taps(raw.w + ((int64_t)(2 * H + h) * DK + 8 * lr) * 4, tap);
     uint4 wr[7];
+    if (n == C && t0 - 3 >= q0) {  // a full chunk with its whole window inside the sequence: one stride apart
+        const uint16_t *p = raw.xv + (t0 + 4 * i4 - 3) * rs + col + 8 * lr;
 #pragma unroll
-    for (int m = 0; m < 7; ++m) {
-        const uint16_t *p = src(raw.xv, 2, 4 * i4 - 3 + m);
-        wr[m] = p ? V::load(p + 8 * lr) : V::zero();
+        for (int m = 0; m < 7; ++m) wr[m] = V::load(p + m * rs);
+    } else {
+#pragma unroll
+        for (int m = 0; m < 7; ++m) {
+            const uint16_t *p = src(raw.xv, 2, 4 * i4 - 3 + m);
+            wr[m] = p ? V::load(p + 8 * lr) : V::zero();
+        }
     }
     // q, k rows of the chunk -> the row tiles
-    dma_rows(S.QT, raw.xq + t0 * rs + col, rs, n, lane, wave, 4);
-    dma_rows(S.KL, raw.xk + t0 * rs + col, rs, n, lane, wave, 4);
+    dma_rows(S.QT, raw.xq + t0 * rs + col, rs, n, lane, wave);
+    dma_rows(S.KL, raw.xk + t0 * rs + col, rs, n, lane, wave);
     // the rows in front of the chunk (threads 0 .. 95: tensor, row, 16-byte unit)
     uint4 fr = V::zero();
     if (tid < 96) {
@@ -948,8 +966,8 @@ constexpr int CHAIN_NW = 4;
 __global__ __launch_bounds__(128 * CHAIN_NW) void k_chunk_chain(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ seq_order,
-    int n_seq, int64_t total_tokens, int H, const float *initial_state, float *__restrict__ o, float *final_state,
-    const char *__restrict__ recs) {
+    int n_seq, int64_t total_tokens, int H, int cl, const float *initial_state, float *__restrict__ o,
+    float *final_state, const char *__restrict__ recs) {
     constexpr int NW = CHAIN_NW;
     constexpr int TILES = DK / (16 * NW);
     const int bid = blockIdx.x;
@@ -961,7 +979,7 @@ __global__ __launch_bounds__(128 * CHAIN_NW) void k_chunk_chain(
     const int s = seq_order ? seq_order[rank] : rank;
     const int64_t seq_t0 = cu ? cu[s] : 0;
     const int64_t L = cu ? (int64_t)cu[s + 1] - seq_t0 : total_tokens;
-    const int nc = (int)((L + C - 1) / C);
+    const int nc = (int)((L + cl - 1) / cl);
     const int64_t cb = cu ? chunk_base[s] : 0;
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
@@ -976,8 +994,8 @@ __global__ __launch_bounds__(128 * CHAIN_NW) void k_chunk_chain(
             // releases chunk c to the compute waves (the last one only pairs
             // with their final barrier).
             if (c < nc) {
-                const int64_t t0 = seq_t0 + (int64_t)c * C;
-                const int n = (int)min((int64_t)C, L - (int64_t)c * C);
+                const int64_t t0 = seq_t0 + (int64_t)c * cl;
+                const int n = (int)min((int64_t)cl, L - (int64_t)c * cl);
                 const int64_t rowbase = (t0 * H + h) * DK;
                 chain_copies(buf[c & 1], recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q + rowbase,
                              k + rowbase, v + rowbase, rs, n, lane, cw, NW, 0, CHAIN_PIECES);
@@ -999,8 +1017,8 @@ __global__ __launch_bounds__(128 * CHAIN_NW) void k_chunk_chain(
 
     lds_barrier();  // chunk 0 is in buf[0]
     for (int c = 0; c < nc; ++c) {
-        const int64_t t0 = seq_t0 + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, L - (int64_t)c * C);
+        const int64_t t0 = seq_t0 + (int64_t)c * cl;
+        const int n = (int)min((int64_t)cl, L - (int64_t)c * cl);
         const ChainBuf &B = buf[c & 1];
         const u32x4_t *Twh = reinterpret_cast<const u32x4_t *>(B.rec + REC_TW_HI);
         const u32x4_t *Twl = reinterpret_cast<const u32x4_t *>(B.rec + REC_TW_LO);
@@ -1212,8 +1230,8 @@ template <int MODE>
 __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ seq_order,
-    int n_seq, int64_t total_tokens, int H, const float *initial_state, float *__restrict__ o, float *final_state,
-    const char *__restrict__ recs, float *__restrict__ final_m) {
+    int n_seq, int64_t total_tokens, int H, int cl, const float *initial_state, float *__restrict__ o,
+    float *final_state, const char *__restrict__ recs, float *__restrict__ final_m) {
     const int bid = blockIdx.x;
     // All workgroups of one (sequence, head) share bid % 8, so they run on one XCD and share its L2.
     const int u = (bid / (8 * CS_TILES)) * 8 + (bid & 7);
@@ -1223,7 +1241,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     const int s = seq_order ? seq_order[rank] : rank;
     const int64_t seq_t0 = cu ? cu[s] : 0;
     const int64_t L = cu ? (int64_t)cu[s + 1] - seq_t0 : total_tokens;
-    const int nc = (int)((L + C - 1) / C);
+    const int nc = (int)((L + cl - 1) / cl);
     const int64_t cb = cu ? chunk_base[s] : 0;
     const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops and branches scalar
@@ -1237,8 +1255,8 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     if (wave >= 4) {  // copy wave
         const int cw = wave - 4;
         auto copies = [=](int c, int half) {
-            const int64_t t0 = seq_t0 + (int64_t)c * C;
-            const int n = (int)min((int64_t)C, L - (int64_t)c * C);
+            const int64_t t0 = seq_t0 + (int64_t)c * cl;
+            const int n = (int)min((int64_t)cl, L - (int64_t)c * cl);
             const int64_t rowbase = (t0 * H + h) * DK;
             cs_copies(sm.buf[c & 1], sm.scratch, recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q + rowbase,
                       k + rowbase, v + rowbase + vcol0, rs, rs, n, lane, cw, half);
@@ -1251,8 +1269,8 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         auto touch = [=](int c) {
             int line = tile + CS_TILES * (cw * 64 + lane);
             if (line >= PF_LINES) line = 0;
-            const int64_t t0 = seq_t0 + (int64_t)c * C;
-            const int n = (int)min((int64_t)C, L - (int64_t)c * C);
+            const int64_t t0 = seq_t0 + (int64_t)c * cl;
+            const int n = (int)min((int64_t)cl, L - (int64_t)c * cl);
             const uint32_t *src = chunk_line(recs + ((cb + c) * H + h) * (int64_t)REC_BYTES, q, k, v,
                                              (t0 * H + h) * DK, rs, n, line);
             __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)sm.scratch, 16, 0, 0);
@@ -1320,8 +1338,8 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     // the previous chunk's own output tiles, waiting for the partner's partial Q S0^T
     f32x4_t Oa = zero4(), Oz = zero4();
     auto store_outputs = [&](int cprev) {
-        const int64_t t0 = seq_t0 + (int64_t)cprev * C;
-        const int n = (int)min((int64_t)C, L - (int64_t)cprev * C);
+        const int64_t t0 = seq_t0 + (int64_t)cprev * cl;
+        const int n = (int)min((int64_t)cl, L - (int64_t)cprev * cl);
         float *ob = o + t0 * rs + h * DK;  // o is stored non-temporally (measured about 3% faster)
         const int slot = 4 + 2 * (cprev & 1);
         const f32x4_t fa = Oa + sm.xch[partner][slot][lane], fz = Oz + sm.xch[partner][slot + 1][lane];
@@ -1490,7 +1508,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
 // batch without tokens, when nothing is stored to it); final_m != NULL: the
 // pair of states into final_state and final_m (CS_PAIR; o is not used).
 hipError_t launch_chain_cs(const void *q, const void *k, const void *v, const int32_t *cu, const int32_t *chunk_base,
-                           const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H,
+                           const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H, int cl,
                            const float *initial_state, float *o, float *final_state, const char *recs,
                            hipStream_t stream, float *final_m = nullptr) {
     const int64_t units = n_seq * H;
@@ -1499,12 +1517,12 @@ hipError_t launch_chain_cs(const void *q, const void *k, const void *v, const in
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), cu, chunk_base, seq_order, (int)n_seq, total_tokens, H,
-                       initial_state, o, final_state, recs, final_m);
+                       cl, initial_state, o, final_state, recs, final_m);
     return hipGetLastError();
 }
 
 hipError_t launch_chain(const void *q, const void *k, const void *v, const int32_t *cu, const int32_t *chunk_base,
-                        const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H,
+                        const int32_t *seq_order, int64_t n_seq, int64_t total_tokens, int H, int cl,
                         const float *initial_state, float *o, float *final_state, const char *recs,
                         hipStream_t stream) {
     constexpr int NW = CHAIN_NW;
@@ -1514,7 +1532,7 @@ hipError_t launch_chain(const void *q, const void *k, const void *v, const int32
     hipLaunchKernelGGL(k_chunk_chain, dim3((unsigned)grid), dim3(128 * NW), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), cu, chunk_base, seq_order,
-                       (int)n_seq, total_tokens, H, initial_state, o, final_state, recs);
+                       (int)n_seq, total_tokens, H, cl, initial_state, o, final_state, recs);
     return hipGetLastError();
 }
 
@@ -1647,10 +1665,10 @@ __global__ __launch_bounds__(512) void k_scan_combine(int n_seq, int H, const in
 // a chunk (none is empty), and, when the state is updated in place, no
 // sequence spans two chunks (its one workgroup reads the starting state
 // before it writes the returned one; across workgroups nothing orders them).
-bool layer_state_here(const int32_t *cu_host, int64_t n_seq, int64_t N, bool in_place) {
+bool layer_state_here(const int32_t *cu_host, int64_t n_seq, int64_t N, bool in_place, int cl) {
     for (int64_t s = 0; s < n_seq; ++s) {
         const int64_t len = cu_host ? (int64_t)cu_host[s + 1] - cu_host[s] : N;
-        if (len == 0 || (in_place && len > C)) return false;
+        if (len == 0 || (in_place && len > cl)) return false;
     }
     return n_seq > 0;
 }
@@ -1661,16 +1679,16 @@ bool use_column_split(int64_t sum_chunks, int64_t max_chunks, int64_t n_long, in
 
 }  // namespace
 
-size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H, int mode) {
-    return ws_layout(total_tokens, n_seq, H, scan_possible(mode, n_seq, H)).total;
+size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H, int mode, int cl) {
+    return ws_layout(total_tokens, n_seq, H, cl == C && scan_possible(mode, n_seq, H), cl).total;
 }
 
 // The largest launches: the column-split chain (CS_TILES workgroups of 512
 // per (sequence, head), rounded up to groups of 8 pairs; the other chain forms
 // launch fewer work-items) and k_chunk_prep (one workgroup of 256 per (chunk, head)).
-bool prefill_chunked_fits(int64_t total_tokens, int64_t n_seq, int H) {
+bool prefill_chunked_fits(int64_t total_tokens, int64_t n_seq, int H, int cl) {
     const int64_t units8 = (n_seq * H + 7) / 8 * 8;
-    const int64_t chunks = (total_tokens + C - 1) / C + n_seq;  // at least the sum over sequences
+    const int64_t chunks = (total_tokens + cl - 1) / cl + n_seq;  // at least the sum over sequences
     return launch_fits(units8 * CS_TILES, 512) && launch_fits(chunks * H, 256);
 }
 
@@ -1682,9 +1700,11 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
                                   const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int64_t n_seq,
                                   int64_t total_tokens, int H, const float *initial_state, float *o,
                                   float *final_state, void *workspace, int erase, int mode,
-                                  const hipEvent_t *marks, hipStream_t stream, const LayerRaw *raw) {
-    if (!prefill_chunked_fits(total_tokens, n_seq, H)) return hipErrorInvalidConfiguration;
-    const WsLayout L = ws_layout(total_tokens, n_seq, H, scan_possible(mode, n_seq, H));
+                                  const hipEvent_t *marks, hipStream_t stream, const LayerRaw *raw, int cl) {
+    if (cl != 16 && cl != 32 && cl != C) return hipErrorInvalidValue;
+    if (cl != C && mode == CHUNKED_SCAN) return hipErrorInvalidValue;  // the scan's segments are cut in 64-token chunks
+    if (!prefill_chunked_fits(total_tokens, n_seq, H, cl)) return hipErrorInvalidConfiguration;
+    const WsLayout L = ws_layout(total_tokens, n_seq, H, cl == C && scan_possible(mode, n_seq, H), cl);
     ScanPlan sp;
     if (L.scan_cap > 0 && plan_scan(cu_seqlens_host, n_seq, total_tokens, H, mode == CHUNKED_SCAN, sp) &&
         sp.P > L.scan_cap)
@@ -1700,17 +1720,18 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     if (cu_seqlens) {
         n_long = 0;
         for (int64_t s = 0; s < n_seq; ++s) {
-            const int64_t nc = (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + C - 1) / C;
+            const int64_t nc = (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + cl - 1) / cl;
             n_chunks += nc;
             max_chunks = std::max(max_chunks, nc);
         }
         for (int64_t s = 0; s < n_seq; ++s)
-            n_long += 2 * ((cu_seqlens_host[s + 1] - cu_seqlens_host[s] + C - 1) / C) > max_chunks;
-        hipLaunchKernelGGL(k_plan, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens, (int)n_seq, chunk_base, seq_order);
+            n_long += 2 * ((cu_seqlens_host[s + 1] - cu_seqlens_host[s] + cl - 1) / cl) > max_chunks;
+        hipLaunchKernelGGL(k_plan, dim3(1), dim3(PLAN_THREADS), 0, stream, cu_seqlens, (int)n_seq, cl, chunk_base,
+                           seq_order);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else {
-        n_chunks = max_chunks = (total_tokens + C - 1) / C;
+        n_chunks = max_chunks = (total_tokens + cl - 1) / cl;
     }
     ScanSegs segs;
     if (sp.P > 0) {
@@ -1726,17 +1747,18 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
     LayerRaw lr;
     if (raw) {
         lr = *raw;
-        lr.state_here = layer_state_here(cu_seqlens_host, n_seq, total_tokens, raw->st_in && raw->st_in == raw->st_out);
+        lr.state_here =
+            layer_state_here(cu_seqlens_host, n_seq, total_tokens, raw->st_in && raw->st_in == raw->st_out, cl);
     }
     if (n_chunks > 0) {
         if (raw)
             hipLaunchKernelGGL(k_layer_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream, lr, cu_seqlens,
-                               chunk_base, (int)n_seq, total_tokens, H, erase, raw->a_logit != nullptr ? 1 : 0, recs,
-                               segs);
+                               chunk_base, (int)n_seq, total_tokens, H, erase, raw->a_logit != nullptr ? 1 : 0, cl,
+                               recs, segs);
         else
             hipLaunchKernelGGL(k_chunk_prep, dim3((unsigned)(n_chunks * H)), dim3(256), 0, stream,
                                static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), g, beta,
-                               cu_seqlens, chunk_base, (int)n_seq, total_tokens, H, erase, recs, segs);
+                               cu_seqlens, chunk_base, (int)n_seq, total_tokens, H, erase, cl, recs, segs);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1756,7 +1778,7 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
               *Sin = reinterpret_cast<float *>(ws + L.sin_off);
         // A: R_j and M_j in one pass (the segment offsets were written by k_chunk_prep)
         if (e == hipSuccess)
-            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, nullptr, nullptr, R, recs,
+            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, C, nullptr, nullptr, R, recs,
                                 stream, M);
         if (e == hipSuccess) {
             hipLaunchKernelGGL(k_scan_combine, dim3((unsigned)(64 * ((n_seq * H + 7) / 8))), dim3(512), 0, stream,
@@ -1764,12 +1786,12 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v, c
             e = hipGetLastError();
         }
         if (e == hipSuccess)  // D (its final states land in R, no longer needed)
-            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, Sin, o, R, recs, stream);
+            e = launch_chain_cs(q, k, v, seg_cu, seg_base, nullptr, P, total_tokens, H, C, Sin, o, R, recs, stream);
     } else if (use_column_split(n_chunks, max_chunks, n_long, H))
-        e = launch_chain_cs(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
+        e = launch_chain_cs(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, cl, initial_state, o,
                             final_state, recs, stream);
     else
-        e = launch_chain(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, initial_state, o,
+        e = launch_chain(q, k, v, cu_seqlens, chunk_base, seq_order, n_seq, total_tokens, H, cl, initial_state, o,
                          final_state, recs, stream);
     if (e != hipSuccess) return e;
     return record_mark(marks[2], stream);

@@ -18,7 +18,7 @@ inline bool launch_fits(int64_t blocks, int64_t threads) {
 // anything is enqueued).
 bool decode_fits(int d, int64_t BH);
 bool prefill_serial_fits(int d, int64_t n_seq, int H);
-bool prefill_chunked_fits(int64_t total_tokens, int64_t n_seq, int H);
+bool prefill_chunked_fits(int64_t total_tokens, int64_t n_seq, int H, int chunk_len = 64);
 bool preprocess_fits(bool bf16, int d, int64_t n_seq, int64_t total_tokens, int H);
 
 // One decode step for B*H heads (in-place state update).
@@ -55,11 +55,13 @@ struct LayerRaw {
     int state_here;                   // set by the launch: k_layer_prep returns the conv state itself
 };
 
-// Chunkwise-parallel prefill (64-token chunks, d = 128, bf16 q/k/v).
-// Chunked prefill modes: the library's choice, one chain per (sequence, head),
-// or the chunk-level scan (up to 64 sequences cut into segments).
+// Chunkwise-parallel prefill (d = 128, bf16 q/k/v).  chunk_len: tokens per
+// chunk, 64, or 32 or 16 on the same 64-row kernels (each chunk's tiles part
+// filled; the one-chain forms only).  Chunked prefill modes: the library's
+// choice, one chain per (sequence, head), or the chunk-level scan (up to 64
+// sequences cut into segments).
 enum { CHUNKED_AUTO = 0, CHUNKED_CHAIN = 1, CHUNKED_SCAN = 2 };
-size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H, int mode);
+size_t prefill_chunked_workspace_bytes(int64_t total_tokens, int64_t n_seq, int H, int mode, int chunk_len = 64);
 // Whether CHUNKED_SCAN takes this batch: 1 to 64 sequences, at least one token.
 bool prefill_chunked_scan_supported(int64_t n_seq, int64_t total_tokens);
 hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v,
@@ -67,7 +69,8 @@ hipError_t launch_prefill_chunked(const void *q, const void *k, const void *v,
                                   const int32_t *cu_seqlens_host, int64_t n_seq,
                                   int64_t total_tokens, int H, const float *initial_state,
                                   float *o, float *final_state, void *workspace, int erase, int mode,
-                                  const hipEvent_t *marks, hipStream_t stream, const LayerRaw *raw = nullptr);
+                                  const hipEvent_t *marks, hipStream_t stream, const LayerRaw *raw = nullptr,
+                                  int chunk_len = 64);
 
 // The returned conv state of the pre-processing: per sequence, tensor, head
 // and channel, the last three raw inputs (shifted in from st_in for a sequence

@@ -73,6 +73,17 @@ def test_algorithm_choice():
     assert A(7, 128, 128, 0) == 0
     assert A(gdn.GDN_BF16, 128, 128, 17) == 0
     assert A(gdn.GDN_BF16, 128, 128, gdn.CHUNK_SERIAL) == gdn.CHUNK_SERIAL
+    assert A(gdn.GDN_BF16, 128, 128, gdn.CHUNK_16) == gdn.CHUNK_16
+    assert A(gdn.GDN_BF16, 128, 128, gdn.CHUNK_32) == gdn.CHUNK_32
+    assert A(gdn.GDN_FP32, 128, 128, gdn.CHUNK_32) == 0
+    assert A(gdn.GDN_BF16, 64, 64, gdn.CHUNK_16) == 0
+
+
+def test_shorter_chunks_take_more_records():
+    """The workspace holds one record per chunk: 16-token chunks need about
+    four times the records of 64-token ones, and no scan area."""
+    W = lambda c: gdn.prefill_workspace_bytes(4096, 1, 48, 128, 128, gdn.GDN_BF16, c)
+    assert W(gdn.CHUNK_32) > 1.9 * W(gdn.CHUNK_64_CHAIN) and W(gdn.CHUNK_16) > 3.8 * W(gdn.CHUNK_64_CHAIN)
 
 
 def _prefill(**kw):

@@ -244,3 +244,28 @@ def test_scan_refuses_a_batch_without_tokens():
     with pytest.raises(gdn.GdnError) as e:
         gpu_prefill(inp, chunk=gdn.CHUNK_64_SCAN)
     assert e.value.name == "GDN_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("chunk", [gdn.CHUNK_16, gdn.CHUNK_32])
+def test_shorter_chunks_varlen(oracle_lib, chunk):
+    """16- and 32-token chunks on a ragged batch with empty sequences and
+    initial states: against the oracle, and against 64-token chunks (the
+    chunk length changes nothing beyond rounding)."""
+    say("chunk length", chunk, "varlen")
+    inp = w.make_prefill([130, 0, 64, 1, 333, 65, 17, 15, 16, 33], H=5, d=128, seed=61, gate_shift=-1.0,
+                         init_std=0.3)
+    o, s = check(inp, chunk=chunk, what=f"C={chunk}")
+    o64, s64 = gpu_prefill(inp, chunk=gdn.CHUNK_64)
+    eo, es = rel_max_err(o, o64), rel_max_err(s, s64)
+    say(f"  C={chunk} vs C=64: o={eo:.2e} state={es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("chunk", [gdn.CHUNK_16, gdn.CHUNK_32, gdn.CHUNK_64])
+def test_chunk_lengths_full_size(oracle_lib, chunk):
+    """The one-layer prefill shape (T = 4096, H = 48) with slow gates and an
+    initial state, at every chunk length, against the oracle."""
+    say("chunk length", chunk, "T=4096 H=48")
+    inp = w.make_prefill([4096], H=48, d=128, seed=62, gate_shift=-4.0, init_std=0.3, packed=False)
+    check(inp, chunk=chunk, what=f"C={chunk} T=4096")
+

@@ -115,10 +115,10 @@ def test_layer_in_place_states_and_no_gate_outputs(lengths):
     assert_same(got, ref, ("o", "s", "st", "q", "k", "v"), "in place")
 
 
-@pytest.mark.parametrize("chunk", [gdn.CHUNK_64_CHAIN, gdn.CHUNK_64_SCAN])
+@pytest.mark.parametrize("chunk", [gdn.CHUNK_64_CHAIN, gdn.CHUNK_64_SCAN, gdn.CHUNK_32, gdn.CHUNK_16])
 def test_layer_chunk_forms(chunk):
-    """The per-pair chain and the chunk-level scan (segments) behind the fused
-    preparation."""
+    """The per-pair chain, the chunk-level scan (segments) and the shorter
+    chunks behind the fused preparation."""
     say("layer chunk form", chunk)
     inp = w.make_preprocess([900, 77], H=2, d=128, dtype="bf16", seed=22, activation="silu")
     d = dev_inputs(inp)
