@@ -33,22 +33,27 @@ struct RowLayout {
 };
 
 // ---------------------------------------------------------------------------
-// Decode: grid = B*H workgroups of NW waves; wave w owns rows [w*D/NW, (w+1)*D/NW).
+// Decode: grid = B*H*SPLIT workgroups of NW waves; workgroup part p of a
+// (row, head) owns its rows [p*D/SPLIT, (p+1)*D/SPLIT), and wave w of it a
+// 1/NW share of those.  Splitting a head's rows over workgroups keeps each
+// lane's loads in flight to a few (as a copy kernel streams best).
 // NT: stream the state with non-temporal loads and stores (large batches).
 // slots: NULL for state [B][H][dv][dk]; else row b of the batch uses state
 // slot slots[b] of a pool [n_slots][H][dv][dk], and a row whose slot lies
 // outside [0, n_slots) is padding: its o row is zeroed, no state is touched.
 // g == NULL: no gate (g = 1).  erase == 0: no recall term (c = beta v).
-template <typename TIn, int D, int NW, bool NT>
+template <typename TIn, int D, int NW, int SPLIT, bool NT>
 __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                          const TIn *__restrict__ v, const float *__restrict__ g,
                                                          const float *__restrict__ beta, float *__restrict__ state,
                                                          float *__restrict__ o, const int32_t *__restrict__ slots,
                                                          int64_t n_slots, int H, int erase) {
     using L = RowLayout<D>;
-    constexpr int RPW = D / NW;
+    constexpr int RPG = D / SPLIT;  // rows of this workgroup
+    constexpr int RPW = RPG / NW;
     constexpr int PASSES = (RPW + L::RPP - 1) / L::RPP;
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = blockIdx.x / SPLIT;
+    const int row0 = (int)(blockIdx.x % SPLIT) * RPG;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane % L::LPR, rs = lane / L::LPR;
     const int c0 = 4 * lr, c1 = D / 2 + 4 * lr;
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__
         const int64_t b = bh / H;
         const int32_t slot = slots[b];
         if (slot < 0 || slot >= n_slots) {  // padding row (uniform across the workgroup)
-            for (int i = threadIdx.x; i < D; i += 64 * NW) o[bh * D + i] = 0.f;
+            for (int i = threadIdx.x; i < RPG; i += 64 * NW) o[bh * D + row0 + i] = 0.f;
             return;
         }
         sh = (int64_t)slot * H + (bh - b * H);
@@ -76,7 +81,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__
     for (int p = 0; p < PASSES; ++p) {
         const int rloc = p * L::RPP + rs;
         const bool ok = rloc < RPW;
-        const int row = wave * RPW + (ok ? rloc : 0);
+        const int row = row0 + wave * RPW + (ok ? rloc : 0);
         if (ok) {
             s0[p] = load_state4<NT>(S + row * D + c0);
             s1[p] = load_state4<NT>(S + row * D + c1);
@@ -90,7 +95,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__
     for (int p = 0; p < PASSES; ++p) {
         const int rloc = p * L::RPP + rs;
         const bool ok = rloc < RPW;
-        const int row = wave * RPW + rloc;
+        const int row = row0 + wave * RPW + rloc;
         const float a = group_sum<L::LPR>(dot4(s0[p], k0) + dot4(s1[p], k1));
         const float b = group_sum<L::LPR>(dot4(s0[p], q0) + dot4(s1[p], q1));
         const float c = bt * (vr[p] - (erase ? a : 0.f));
@@ -196,23 +201,31 @@ constexpr int64_t DECODE_NT_MIN_BYTES = int64_t(32) << 20;
 
 // waves per decode workgroup; row tiles (workgroups) per (sequence, head) of the serial prefill
 static constexpr int decode_waves(int d) { return d >= 64 ? 4 : 1; }
+// Workgroups per (row, head): the d = 128 state's 128 rows in four parts of
+// 32, four 16-byte loads in flight per lane.  Measured on 64 rows x 48 heads:
+// one workgroup per head 67.3 us per step, two 65.9, four 62.6, eight 73.1 (a
+// plain copy kernel streams best with about four loads per lane and many
+// workgroups, too).
+static constexpr int decode_split(int d) { return d == 128 ? 4 : 1; }
 static constexpr int serial_tiles(int d) { return d >= 32 ? d / 32 : 1; }
 
-bool decode_fits(int d, int64_t BH) { return launch_fits(BH, 64 * decode_waves(d)); }
+bool decode_fits(int d, int64_t BH) { return launch_fits(BH * decode_split(d), 64 * decode_waves(d)); }
 bool prefill_serial_fits(int d, int64_t n_seq, int H) { return launch_fits(n_seq * H * serial_tiles(d), 64); }
 
 template <typename TIn, int D>
 static hipError_t decode_d(const void *q, const void *k, const void *v, const float *g, const float *beta,
                            float *state, float *o, int64_t BH, int H, const int32_t *slots, int64_t n_slots,
                            int erase, hipStream_t stream) {
-    constexpr int NW = decode_waves(D);
+    constexpr int NW = decode_waves(D), SPLIT = decode_split(D);
     if (!decode_fits(D, BH)) return hipErrorInvalidConfiguration;
     if (BH * D * D * 4 >= DECODE_NT_MIN_BYTES)
-        hipLaunchKernelGGL((k_decode_step<TIn, D, NW, true>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
+        hipLaunchKernelGGL((k_decode_step<TIn, D, NW, SPLIT, true>), dim3((unsigned)(BH * SPLIT)), dim3(64 * NW), 0,
+                           stream,
                            (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o, slots, n_slots, H,
                            erase);
     else
-        hipLaunchKernelGGL((k_decode_step<TIn, D, NW, false>), dim3((unsigned)BH), dim3(64 * NW), 0, stream,
+        hipLaunchKernelGGL((k_decode_step<TIn, D, NW, SPLIT, false>), dim3((unsigned)(BH * SPLIT)), dim3(64 * NW), 0,
+                           stream,
                            (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, state, o, slots, n_slots, H,
                            erase);
     return hipGetLastError();
