@@ -546,29 +546,30 @@ __device__ __forceinline__ void prep_body(PrepSmem &S, char *__restrict__ rec, i
     lds_barrier();  // L complete
 
     // T = (I + L)^{-1} by 16x16 blocks.  Diagonal blocks D_a = (I + L_aa)^{-1}:
-    // wave a, lane c solves column c by forward substitution from registers.
-    {
-        const int a = wave, c = lane & 15;
-        float lb[16][16];
-#pragma unroll
-        for (int t = 1; t < 16; ++t)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 x = t4(S.KL, 16 * a + t, 16 * a + 4 * q4);
-                lb[t][4 * q4] = x.x; lb[t][4 * q4 + 1] = x.y; lb[t][4 * q4 + 2] = x.z; lb[t][4 * q4 + 3] = x.w;
-            }
+    // one wave, lane (a, c) solves column c of block a by forward substitution
+    // from registers (one lane per column: the other waves would only repeat
+    // the same instructions).  The solving wave differs from workgroup to
+    // workgroup, so that the co-resident workgroups of a CU spread it over
+    // their SIMDs.
+    if (wave == (int)(blockIdx.x & 3)) {
+        const int a = g4, c = r;
         float x[16];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t = 0; t < 16; ++t) {  // row t of the block, read as it is needed
+            float lt[16];
+#pragma unroll
+            for (int q4 = 0; q4 < (t + 3) / 4; ++q4) {
+                const float4 y = t4(S.KL, 16 * a + t, 16 * a + 4 * q4);
+                lt[4 * q4] = y.x; lt[4 * q4 + 1] = y.y; lt[4 * q4 + 2] = y.z; lt[4 * q4 + 3] = y.w;
+            }
             float acc = (t == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int rr = 0; rr < t; ++rr) acc -= lb[t][rr] * x[rr];
+            for (int rr = 0; rr < t; ++rr) acc -= lt[rr] * x[rr];
             x[t] = acc;
         }
-        if (lane < 16) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) *tref(S.QT, 16 * a + t, 16 * a + c) = x[t];
-        } else if (lane < 32 && (a == 0 || a == 2)) {  // upper blocks inside the 32-wide fragment steps are zero
+        for (int t = 0; t < 16; ++t) *tref(S.QT, 16 * a + t, 16 * a + c) = x[t];
+        if (a == 0 || a == 2) {  // upper blocks inside the 32-wide fragment steps are zero
 #pragma unroll
             for (int t = 0; t < 16; ++t) *tref(S.QT, 16 * a + t, 16 * a + 16 + c) = 0.f;
         }
