@@ -457,6 +457,80 @@ struct ScanSegs {
 // Everything of a chunk's preparation once its q and k rows are on their way
 // into (or in) the row tiles S.QT and S.KL: wave 0 holds the chunk's gates gl
 // (g, unless has_g is false) and bl (beta) for token min(lane, n - 1).
+// Five 16x16 tiles of one wave: for row blocks RA and RB, the tiles (RA, sa),
+// sa = 0..RA, then (RB, sa), sa = 0..RB.  P_TILES false: K K^T tiles, masked
+// and decayed into L, lane (g, r) holding L[16 ta + 4 g + e][16 sa + r];
+// true: tiles of P, lane (g, r) holding P[16 tb + r][16 sa + 4 g + e].  Each
+// k step reads the fragments of k's row blocks 0..RA (and of q's rows RA, RB)
+// once and feeds them to every tile, so the wave reads each fragment once.
+template <int RA, int RB, bool P_TILES>
+__device__ __forceinline__ void gram_tiles(PrepSmem &S, int g4, int r, int erase, f32x4_t (&out)[5]) {
+    static_assert(RA + RB + 2 == 5, "five tiles per wave");
+    f32x4_t acc[5];
+#pragma unroll
+    for (int x = 0; x < 5; ++x) acc[x] = zero4();
+#pragma unroll
+    for (int kj = 0; kj < 4; ++kj) {
+        u32x4_t kf[RA + 1];
+#pragma unroll
+        for (int bk = 0; bk <= RA; ++bk) kf[bk] = rowfrag(S.KL, 16 * bk, kj, g4, r);
+        u32x4_t qa, qb;
+        if (P_TILES) {
+            qa = rowfrag(S.QT, 16 * RA, kj, g4, r);
+            qb = rowfrag(S.QT, 16 * RB, kj, g4, r);
+        }
+#pragma unroll
+        for (int sa = 0; sa <= RA; ++sa) acc[sa] = P_TILES ? mfma(kf[sa], qa, acc[sa]) : mfma(kf[RA], kf[sa], acc[sa]);
+#pragma unroll
+        for (int sa = 0; sa <= RB; ++sa)
+            acc[RA + 1 + sa] = P_TILES ? mfma(kf[sa], qb, acc[RA + 1 + sa]) : mfma(kf[RB], kf[sa], acc[RA + 1 + sa]);
+    }
+#pragma unroll
+    for (int x = 0; x < 5; ++x) {
+        const int ta = x <= RA ? RA : RB, sa = x <= RA ? x : x - RA - 1;
+        f32x4_t v = acc[x];
+        if (!P_TILES) {
+            const int s = 16 * sa + r;
+            const float gs = S.G[s], bs = S.B[s];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * ta + 4 * g4 + e;
+                const float gtm1 = t > 0 ? S.G[t - 1] : 0.f;
+                v[e] = (s < t && erase) ? bs * __expf(gtm1 - gs) * v[e] : 0.f;
+            }
+        } else {
+            const int t = 16 * ta + r;
+            const float Gt = S.G[t];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sx = 16 * sa + 4 * g4 + e;
+                v[e] = sx <= t ? S.B[sx] * __expf(Gt - S.G[sx]) * v[e] : 0.f;
+            }
+        }
+        out[x] = v;
+    }
+}
+
+template <int RA, int RB>
+__device__ __forceinline__ void put_l_tiles(PrepSmem &S, int g4, int r, const f32x4_t (&L)[5]) {
+#pragma unroll
+    for (int x = 0; x < 5; ++x) {
+        const int ta = x <= RA ? RA : RB, sa = x <= RA ? x : x - RA - 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *tref(S.KL, 16 * ta + 4 * g4 + e, 16 * sa + r) = L[x][e];
+    }
+}
+
+template <int RA, int RB>
+__device__ __forceinline__ void put_p_tiles(PrepSmem &S, int g4, int r, const f32x4_t (&P)[5]) {
+#pragma unroll
+    for (int x = 0; x < 5; ++x) {
+        const int tb = x <= RA ? RA : RB, sa = x <= RA ? x : x - RA - 1;
+        *reinterpret_cast<float4 *>(tref(S.KL, 16 * tb + r, 16 * sa + 4 * g4)) =
+            make_float4(P[x][0], P[x][1], P[x][2], P[x][3]);
+    }
+}
+
 __device__ __forceinline__ void prep_body(PrepSmem &S, char *__restrict__ rec, int n, float gl, float bl, bool has_g,
                                           int erase, int wave, int lane, int g4, int r) {
     float f_eg = 0.f, f_egm1 = 0.f, f_egn = 0.f;  // the record's gate factors (wave 0)
@@ -483,66 +557,19 @@ __device__ __forceinline__ void prep_body(PrepSmem &S, char *__restrict__ rec, i
         if (lane == 63) gate[GATE_EGN] = f_egn;
     }
 
-    // K K^T tiles (the 10 tiles on and below the diagonal; item i = wave + 4 j,
-    // i < 10, kept in registers until k's tile may be overwritten) and the
-    // blocks of P (items 10..15: block i - 10, its two 16x16 halves kept in
-    // registers as fp32 until P T is formed).  Lane (g, r) of a P half holds
-    // P[16 tb + r][16 sa + 4 g + e].
-    f32x4_t Lr[3], Pr[2][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = wave + 4 * j;
-        if (i < 10) {
-            const int ta = i >= 6 ? 3 : i >= 3 ? 2 : i >= 1 ? 1 : 0;
-            const int sa = i - ta * (ta + 1) / 2;
-            f32x4_t acc = zero4();
-#pragma unroll
-            for (int kj = 0; kj < 4; ++kj)
-                acc = mfma(rowfrag(S.KL, 16 * ta, kj, g4, r), rowfrag(S.KL, 16 * sa, kj, g4, r), acc);
-            const int s = 16 * sa + r;
-            const float gs = S.G[s], bs = S.B[s];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * ta + 4 * g4 + e;
-                const float gtm1 = t > 0 ? S.G[t - 1] : 0.f;
-                acc[e] = (s < t && erase) ? bs * __expf(gtm1 - gs) * acc[e] : 0.f;
-            }
-            if (j < 3) Lr[j] = acc;
-        } else if (i < 16) {
-            const int pb = i - 10;
-            const int tb = pb < 2 ? pb : 2 + ((pb - 2) >> 1), ks = pb < 2 ? 0 : ((pb - 2) & 1);
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int sa = 2 * ks + half;
-                f32x4_t p = zero4();
-                if (sa <= tb) {
-                    f32x4_t acc = zero4();
-#pragma unroll
-                    for (int kj = 0; kj < 4; ++kj)
-                        acc = mfma(rowfrag(S.KL, 16 * sa, kj, g4, r), rowfrag(S.QT, 16 * tb, kj, g4, r), acc);
-                    const int t = 16 * tb + r;
-                    const float Gt = S.G[t];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int sx = 16 * sa + 4 * g4 + e;
-                        p[e] = sx <= t ? S.B[sx] * __expf(Gt - S.G[sx]) * acc[e] : 0.f;
-                    }
-                }
-                if (j >= 2) Pr[j - 2][half] = p;
-            }
-        }
-    }
+    // K K^T tiles (the 10 on and below the diagonal) and the tiles of P, five
+    // per wave: waves 0, 1 the K K^T tiles of row blocks {3, 0} and {2, 1},
+    // waves 2, 3 the P tiles of the same row blocks (gram_tiles).  The K K^T
+    // tiles are kept in registers until k's tile may be overwritten, the P
+    // tiles as fp32 until P T is formed.
+    f32x4_t Tl[5];
+    if (wave == 0) gram_tiles<3, 0, false>(S, g4, r, erase, Tl);
+    else if (wave == 1) gram_tiles<2, 1, false>(S, g4, r, erase, Tl);
+    else if (wave == 2) gram_tiles<3, 0, true>(S, g4, r, erase, Tl);
+    else gram_tiles<2, 1, true>(S, g4, r, erase, Tl);
     lds_barrier();  // k and q are no longer needed: their tiles become L and T
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int i = wave + 4 * j;
-        if (i < 10) {
-            const int ta = i >= 6 ? 3 : i >= 3 ? 2 : i >= 1 ? 1 : 0;
-            const int sa = i - ta * (ta + 1) / 2;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) *tref(S.KL, 16 * ta + 4 * g4 + e, 16 * sa + r) = Lr[j][e];
-        }
-    }
+    if (wave == 0) put_l_tiles<3, 0>(S, g4, r, Tl);
+    else if (wave == 1) put_l_tiles<2, 1>(S, g4, r, Tl);
     lds_barrier();  // L complete
 
     // T = (I + L)^{-1} by 16x16 blocks.  Diagonal blocks D_a = (I + L_aa)^{-1}:
@@ -626,23 +653,8 @@ __device__ __forceinline__ void prep_body(PrepSmem &S, char *__restrict__ rec, i
     }
 
     // P (fp32) into the L tile, for the product P T
-#pragma unroll
-    for (int j = 2; j < 4; ++j) {
-        const int i = wave + 4 * j;
-        if (i >= 10 && i < 16) {
-            const int pb = i - 10;
-            const int tb = pb < 2 ? pb : 2 + ((pb - 2) >> 1), ks = pb < 2 ? 0 : ((pb - 2) & 1);
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int sa = 2 * ks + half;
-                if (sa <= tb) {
-                    const f32x4_t p = Pr[j - 2][half];
-                    *reinterpret_cast<float4 *>(tref(S.KL, 16 * tb + r, 16 * sa + 4 * g4)) =
-                        make_float4(p[0], p[1], p[2], p[3]);
-                }
-            }
-        }
-    }
+    if (wave == 2) put_p_tiles<3, 0>(S, g4, r, Tl);
+    else if (wave == 3) put_p_tiles<2, 1>(S, g4, r, Tl);
     // Tw fragments: block tblk(tb, ks), lane (g, r) holds
     // beta_t e^{G_n - G_t} T[t][32 ks + slot_k(g, e)], t = 16 tb + r, split hi/lo
     for (int pb = wave; pb < T_BLOCKS; pb += 4) {
