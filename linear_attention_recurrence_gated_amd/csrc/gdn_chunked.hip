@@ -1348,8 +1348,12 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
     const int ta = hf ? 1 : 0, tz = hf ? 2 : 3;
     const int pa = hf ? 0 : 1, pz = hf ? 3 : 2;
     const int ooff = 4 * g4 * rs + iw + r;
-    // the previous chunk's own output tiles, waiting for the partner's partial Q S0^T
+    // the previous chunk's own output tiles, waiting for the partner's partial Q S0^T,
+    // and the operands they are formed from at the top of the next chunk:
+    // its (P T) fragments, Y and this wave's partial e^{G_t} Q S0^T of its tiles
     f32x4_t Oa = zero4(), Oz = zero4();
+    u32x4_t pah = {}, pal = {}, pz0h = {}, pz0l = {}, pz1h = {}, pz1l = {}, yh0 = {}, yl0 = {}, yh1 = {}, yl1 = {};
+    f32x4_t qsa = zero4(), qsz = zero4();
     auto store_outputs = [&](int cprev) {
         const int64_t t0 = seq_t0 + (int64_t)cprev * cl;
         const int n = (int)min((int64_t)cl, L - (int64_t)cprev * cl);
@@ -1395,6 +1399,14 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             sm.xch[wave][tb][lane] = X[tb];
             if (pair) sm.xch[wave][4 + tb][lane] = Xm[tb];
         }
+        // the previous chunk's own output tiles: e^{G_t} Q S0^T (own columns) + (P T) Y,
+        // formed while this chunk's partial products wait on their operands
+        if (outs) {
+            Oa = mfma_p<PREC_PTY>(pah, pal, yh0, yl0, qsa);
+            Oz = mfma_p<PREC_PTY>(pz0h, pz0l, yh0, yl0, qsz);
+            Oz = mfma_p<PREC_PTY>(pz1h, pz1l, yh1, yl1, Oz);
+            if (c > 0) store_outputs(c - 1);
+        }
         lds_barrier();  // X_c: partials visible
 
         // Tw and this wave's (P T) blocks: the buffer is stable until A_{c+1}
@@ -1405,7 +1417,6 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             tfl[bk] = Twl[bk * 64 + lane];
         }
         const int bz = tblk(tz, 0);  // tile tz in {2, 3} has blocks bz, bz + 1; tile ta in {0, 1} is block ta
-        u32x4_t pah, pal, pz0h, pz0l, pz1h, pz1l;
         if (outs) {
             pah = PTh[ta * 64 + lane];
             pal = PTl[ta * 64 + lane];
@@ -1466,17 +1477,19 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
                 if (pair) Wm[tb] = mfma_p<PREC_TWY>(tfh[tblk(tb, ks)], tfl[tblk(tb, ks)], bYmh[ks], bYml[ks], Wm[tb]);
             }
         }
-        // the previous chunk's outputs (the partner's partials of it are in
-        // the other parity's slots), then this chunk's own output tiles:
-        // e^{G_t} Q S0^T (own columns) + (P T) Y
+        // this chunk's partials of the partner's tiles pa, pz (the partner
+        // completes them next chunk; the other parity's slots still hold the
+        // previous chunk's); its own tiles are formed at the top of the next chunk
         if (outs) {
-            if (c > 0) store_outputs(c - 1);
             const int slot = 4 + 2 * (c & 1);
-            sm.xch[wave][slot][lane] = QS[2];  // the partner's tiles pa, pz
+            sm.xch[wave][slot][lane] = QS[2];
             sm.xch[wave][slot + 1][lane] = QS[3];
-            Oa = mfma_p<PREC_PTY>(pah, pal, bYh[0], bYl[0], QS[0]);
-            Oz = mfma_p<PREC_PTY>(pz0h, pz0l, bYh[0], bYl[0], QS[1]);
-            Oz = mfma_p<PREC_PTY>(pz1h, pz1l, bYh[1], bYl[1], Oz);
+            qsa = QS[0];
+            qsz = QS[1];
+            yh0 = bYh[0];
+            yl0 = bYl[0];
+            yh1 = bYh[1];
+            yl1 = bYl[1];
         }
 
         // S0^T <- e^{G_n} S0^T + K^T W, this wave's 64 columns
@@ -1505,7 +1518,12 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
         }
         lds_barrier();  // A_{c+1}: chunk c + 1 is in the other buffer, this one is free, the partials are visible
     }
-    if (outs && nc > 0) store_outputs(nc - 1);
+    if (outs && nc > 0) {
+        Oa = mfma_p<PREC_PTY>(pah, pal, yh0, yl0, qsa);
+        Oz = mfma_p<PREC_PTY>(pz0h, pz0l, yh0, yl0, qsz);
+        Oz = mfma_p<PREC_PTY>(pz1h, pz1l, yh1, yl1, Oz);
+        store_outputs(nc - 1);
+    }
 
     float *dst = final_state + sbase;
 #pragma unroll
