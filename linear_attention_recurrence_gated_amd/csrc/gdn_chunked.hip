@@ -269,7 +269,28 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---------------------------------------------------------------------------
 // Row tiles in LDS.  Unit u (16 bytes, columns 8u..8u+7) of row t sits at
-// t * 256 + ((u ^ (t & 15)) << 4).
+// t * 256 + ((u ^ key(t)) << 4), the key a function of t & 15: t & 15 in the
+// chunk preparation (its fp32 T layout shares that swizzle), chain_key(t) in
+// the chains.  The chains read their k tiles both by rows (16-byte row
+// fragments) and by the state update's transposing reads, which fetch, per
+// pass of 32 lanes, one 8-byte half of four consecutive units in each of 8
+// rows.  With t & 15 those units of the 8 rows fall on the same 16 banks
+// twice over: 6 conflict cycles per transposing read (counted by the
+// hardware's bank-conflict counter on an in-bounds probe of each pattern).
+// chain_key's bits 3..2 take each value twice in every aligned block of 8
+// rows, which leaves 2, the least with one half per pass; its row-fragment
+// reads take 4 conflict cycles (none with t & 15).  The update is on the
+// chain's serial path: at T = 4096, H = 48 the call measured 2.5 us faster.
+// The q and v tiles take the same key (q's row reads with t & 15 measured
+// 0.9 us slower, though without conflicts; v's transposing reads take 2
+// conflict cycles with either key).
+__device__ __forceinline__ int chain_key(int t) {
+    return ((((t >> 1) ^ t) & 1) << 3) | ((((t >> 2) ^ t) & 1) << 2) | (((t >> 3) & 1) << 1) | (t & 1);
+}
+template <bool CHAIN_TILE>
+__device__ __forceinline__ int row_key(int t) {
+    return CHAIN_TILE ? chain_key(t) : (t & 15);
+}
 
 // Copy 64 token rows (one chunk of one head, rows past n clamped to row n-1)
 // from global memory into a row tile, by a 4-wave workgroup: wave w copies
@@ -297,9 +318,10 @@ __device__ __forceinline__ void dma_rows(char *tile, const uint16_t *chunk, int6
 }
 
 // Row fragment in natural column order: lane (g, r) gets row `row0 + r`, columns 32kj + 8g .. +7.
+template <bool CHAIN_TILE = false>
 __device__ __forceinline__ u32x4_t rowfrag(const char *tile, int row0, int kj, int g4, int r) {
     const int t = row0 + r, u = 4 * kj + g4;
-    return *reinterpret_cast<const u32x4_t *>(tile + t * 256 + ((u ^ (t & 15)) << 4));
+    return *reinterpret_cast<const u32x4_t *>(tile + t * 256 + ((u ^ row_key<CHAIN_TILE>(t)) << 4));
 }
 
 // Columns of the state in the chains' accumulators.  Tile jm of S^T (16
@@ -311,7 +333,7 @@ __device__ __forceinline__ u32x4_t rowfrag(const char *tile, int row0, int kj, i
 __device__ __forceinline__ int st_col(int jm, int g4) { return 32 * (jm >> 1) + 8 * g4 + 4 * (jm & 1); }
 
 // Token-major fragment of the transpose: lane (g, r) gets X[32ks + slot_k(g, e)][16cm + r], e = 0..7,
-// where X is the row tile (tokens x columns).  Two transposing loads of four tokens each (lane
+// where X is a chain row tile (tokens x columns).  Two transposing loads of four tokens each (lane
 // (e, m) of a group of 16 loads columns 4m .. 4m + 3 of token 4g + e; lane r receives column r).
 __device__ __forceinline__ u32x4_t colfrag(const char *tile, int ks, int cm, int g4, int lane) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -319,9 +341,9 @@ __device__ __forceinline__ u32x4_t colfrag(const char *tile, int ks, int cm, int
     const int unit = 2 * cm + (m >> 1), half = (m & 1) * 8;
     const int t0 = 32 * ks + 4 * g4 + e, t1 = t0 + 16;
     const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(tile + t0 * 256 + ((unit ^ (t0 & 15)) << 4) + half));
+        (__attribute__((address_space(3))) v4i16 *)(tile + t0 * 256 + ((unit ^ chain_key(t0)) << 4) + half));
     const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(tile + t1 * 256 + ((unit ^ (t1 & 15)) << 4) + half));
+        (__attribute__((address_space(3))) v4i16 *)(tile + t1 * 256 + ((unit ^ chain_key(t1)) << 4) + half));
     const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
     return u32x4_t{a2[0], a2[1], b2[0], b2[1]};
 }
@@ -336,9 +358,9 @@ __device__ __forceinline__ u32x4_t colfrag_st(const char *tile, int ks, int cm, 
     const int unit = 4 * (cm >> 1) + m, half = (cm & 1) * 8;
     const int t0 = 32 * ks + 4 * g4 + e, t1 = t0 + 16;
     const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(tile + t0 * 256 + ((unit ^ (t0 & 15)) << 4) + half));
+        (__attribute__((address_space(3))) v4i16 *)(tile + t0 * 256 + ((unit ^ chain_key(t0)) << 4) + half));
     const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(tile + t1 * 256 + ((unit ^ (t1 & 15)) << 4) + half));
+        (__attribute__((address_space(3))) v4i16 *)(tile + t1 * 256 + ((unit ^ chain_key(t1)) << 4) + half));
     const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
     return u32x4_t{a2[0], a2[1], b2[0], b2[1]};
 }
@@ -944,10 +966,10 @@ struct ChainBuf {
 };
 constexpr int CHAIN_PIECES = REC_PIECES + 3 * 16;  // one-kilobyte copies per chunk
 
-// Copy one kilobyte (piece a of 16) of a chunk's token rows into a row tile.
+// Copy one kilobyte (piece a of 16) of a chunk's token rows into a chain row tile.
 __device__ __forceinline__ void dma_row_piece(char *tile, const uint16_t *chunk, int rs, int n, int lane, int a) {
     const int t = 4 * a + (lane >> 4);
-    const int u = (lane & 15) ^ (t & 15);
+    const int u = (lane & 15) ^ chain_key(t);
     const uint16_t *src = chunk + (uint32_t)(min(t, n - 1) * rs + 8 * u);
     __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)(tile + a * FRAG), 16, 0, 0);
 }
@@ -1050,8 +1072,8 @@ __global__ __launch_bounds__(128 * CHAIN_NW) void k_chunk_chain(
             O[tb] = zero4();
 #pragma unroll
             for (int kj = 0; kj < 4; ++kj) {
-                X[tb] = mfma_p<PREC_KS>(rowfrag(B.K, 16 * tb, kj, g4, r), u32x4_t{}, bSh[kj], bSl[kj], X[tb]);
-                O[tb] = mfma_p<PREC_KS>(rowfrag(B.Q, 16 * tb, kj, g4, r), u32x4_t{}, bSh[kj], bSl[kj], O[tb]);
+                X[tb] = mfma_p<PREC_KS>(rowfrag<true>(B.K, 16 * tb, kj, g4, r), u32x4_t{}, bSh[kj], bSl[kj], X[tb]);
+                O[tb] = mfma_p<PREC_KS>(rowfrag<true>(B.Q, 16 * tb, kj, g4, r), u32x4_t{}, bSh[kj], bSl[kj], O[tb]);
             }
         }
         // Y = V - diag(e^{G_{t-1}}) X, in accumulator layout (tiles 2 ks and 2 ks + 1 from one V^T fragment)
@@ -1392,7 +1414,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
             Xm[tb] = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const u32x4_t kf = rowfrag(B.K, 16 * tb, 2 * hf + kk, g4, r);
+                const u32x4_t kf = rowfrag<true>(B.K, 16 * tb, 2 * hf + kk, g4, r);
                 X[tb] = mfma_p<PREC_KS>(kf, u32x4_t{}, bSh[kk], bSl[kk], X[tb]);
                 if (pair) Xm[tb] = mfma_p<PREC_KS>(kf, u32x4_t{}, bMh[kk], bMl[kk], Xm[tb]);
             }
@@ -1440,7 +1462,7 @@ __global__ __launch_bounds__(512) void k_chunk_chain_cs(
                 QS[x] = zero4();
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    QS[x] = mfma_p<PREC_KS>(rowfrag(B.Q, 16 * tb, 2 * hf + kk, g4, r), u32x4_t{}, bSh[kk], bSl[kk],
+                    QS[x] = mfma_p<PREC_KS>(rowfrag<true>(B.Q, 16 * tb, 2 * hf + kk, g4, r), u32x4_t{}, bSh[kk], bSl[kk],
                                             QS[x]);
                 QS[x] *= *reinterpret_cast<const f32x4_t *>(gate + GATE_EG + 16 * tb + 4 * g4);
             }

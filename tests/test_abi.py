@@ -335,8 +335,9 @@ def test_launch_size_limits():
         return L.gdn_decode_step(FAKE, FAKE, FAKE, gdn.GDN_BF16, FAKE, FAKE, FAKE * 64, FAKE * 128, B, H, 128, 128,
                                  0, None)
 
-    assert decode(1 << 23, 2) == 2       # 2^24 heads of 256 work-items
-    assert decode((1 << 23) - 1, 2) == 8  # past the size check: o overlaps q
+    # d = 128: four workgroups of 256 work-items per head
+    assert decode(1 << 21, 2) == 2       # 2^22 heads of 1,024 work-items
+    assert decode((1 << 21) - 1, 2) == 8  # past the size check: o overlaps q
     # pre-processing, d = 128 bf16: 3 tensors x ceil(H/16) head groups x ceil(N/16) ranges, 256 work-items each
     st, msg = _preprocess(N=16 * ((1 << 24) // 3 + 1), H=16, d=128)
     assert st == 2 and "exceed one launch" in msg, (st, msg)
