@@ -269,24 +269,26 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---------------------------------------------------------------------------
 // Row tiles in LDS.  Unit u (16 bytes, columns 8u..8u+7) of row t sits at
-// t * 256 + ((u ^ key(t)) << 4), the key a function of t & 15: t & 15 in the
-// chunk preparation (its fp32 T layout shares that swizzle), chain_key(t) in
-// the chains.  The chains read their k tiles both by rows (16-byte row
-// fragments) and by the state update's transposing reads, which fetch, per
-// pass of 32 lanes, one 8-byte half of four consecutive units in each of 8
-// rows.  With t & 15 those units of the 8 rows fall on the same 16 banks
-// twice over: 6 conflict cycles per transposing read (counted by the
-// hardware's bank-conflict counter on an in-bounds probe of each pattern).
-// chain_key's bits 3..2 take each value twice in every aligned block of 8
-// rows, which leaves 2, the least with one half per pass; its row-fragment
-// reads take 4 conflict cycles (none with t & 15).  The update is on the
-// chain's serial path: at T = 4096, H = 48 the call measured 2.5 us faster.
-// The q and v tiles take the same key (q's row reads with t & 15 measured
-// 0.9 us slower, though without conflicts; v's transposing reads take 2
-// conflict cycles with either key).
-__device__ __forceinline__ int chain_key(int t) {
-    return ((((t >> 1) ^ t) & 1) << 3) | ((((t >> 2) ^ t) & 1) << 2) | (((t >> 3) & 1) << 1) | (t & 1);
-}
+// t * 256 + ((u ^ key(t)) << 4), the key a permutation of the row's low four
+// bits: t & 15 in the chunk preparation (its fp32 T layout shares that
+// swizzle), chain_key(t) in the chains.
+//
+// Bank conflicts of the reads, as the hardware's bank-conflict counter shows
+// them on an in-bounds probe of each pattern: a 16-byte read is free of them
+// when the 16 lanes of a group read 16 different units and lanes 2i, 2i + 1
+// read the two halves of one aligned 32-byte pair of units; the chains'
+// transposing reads of the k tile (the state update) fetch, in each pass of
+// 32 lanes, one 8-byte half of four consecutive units in each of 8 rows, so
+// that four units of 8 rows land on 16 banks, at best twice each.  With
+// t & 15 the row-fragment reads are free of conflicts but the transposing
+// reads take 6 conflict cycles each (all four units of the 8 rows on the
+// same banks); chain_key(t), the bits (t2, t1, t3, t0) of t, keeps rows
+// 2i, 2i + 1 on adjacent units (row fragments still free) and takes each
+// value of its bits 3..2 twice in every aligned block of 8 rows, which
+// leaves 2 per transposing read, the least while every lane of a pass reads
+// the same half.  The update is on the chain's serial path: at T = 4096,
+// H = 48 the call measured 154.3 against 159.3 us with t & 15.
+__device__ __forceinline__ int chain_key(int t) { return (((t >> 1) & 3) << 2) | (((t >> 3) & 1) << 1) | (t & 1); }
 template <bool CHAIN_TILE>
 __device__ __forceinline__ int row_key(int t) {
     return CHAIN_TILE ? chain_key(t) : (t & 15);
