@@ -61,9 +61,9 @@ LAYER_QKV_ROUND_TRIP_PER_TOKEN_HEAD = 2 * 3 * D * 2                             
 # Sources each measured kernel is built from: its HBM byte counts (profiles/traffic.json)
 # stay valid while these files are unchanged.
 KERNEL_SOURCES = {
-    "k_chunk_prep": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h", "gdn_conv.h"),
-    "k_chunk_chain": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h", "gdn_conv.h"),
-    "k_layer_prep": ("gdn_chunked.hip", "gdn_mfma.h", "gdn_device.h", "gdn_conv.h"),
+    "k_chunk_prep": ("gdn_chunked.hip", "gdn_chunk_common.h", "gdn_mfma.h", "gdn_device.h", "gdn_conv.h"),
+    "k_chunk_chain": ("gdn_chain.hip", "gdn_chunk_common.h", "gdn_mfma.h", "gdn_device.h", "../build.py"),
+    "k_layer_prep": ("gdn_chunked.hip", "gdn_chunk_common.h", "gdn_mfma.h", "gdn_device.h", "gdn_conv.h"),
     "k_decode_step": ("gdn_rowstream.hip", "gdn_device.h"),
     "k_preprocess": ("gdn_preprocess.hip", "gdn_device.h", "gdn_conv.h"),
 }

@@ -1,8 +1,8 @@
 """Build libgdn.so (gfx950) in-tree from csrc/*.hip with hipcc.
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
-selection switched off and MFMA results kept in ordinary VGPRs, then linked
-into one shared library next to this file.
+selection switched off and MFMA results kept in ordinary VGPRs (plus the
+per-file flags below), then linked into one shared library next to this file.
 """
 import concurrent.futures
 import os
@@ -28,13 +28,21 @@ FLAGS = [
 ]
 
 
+# Per-file flags.  The state chains (one wave per SIMD walking a serial chain
+# of dependent MFMA products) are scheduled for instruction-level parallelism;
+# the other kernels, several workgroups per CU, keep the default scheduler.
+FILE_FLAGS = {
+    "gdn_chain.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
