@@ -109,7 +109,10 @@ __global__ __launch_bounds__(64 * NW) void k_decode_step(const TIn *__restrict__
 
 // ---------------------------------------------------------------------------
 // Token-serial prefill: grid = n_seq * H * (D / ROWS) single-wave workgroups.
-template <typename TIn, int D, int ROWS>
+// Each walks its sequence with the per-token inputs of the next LA tokens in
+// flight (a ring of LA register slots, the loop unrolled by LA), since a
+// token's arithmetic is short next to the latency of its loads.
+template <typename TIn, int D, int ROWS, int LA>
 __global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q, const TIn *__restrict__ k,
                                                        const TIn *__restrict__ v, const float *__restrict__ g,
                                                        const float *__restrict__ beta,
@@ -146,38 +149,45 @@ __global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q
         }
     }
 
-    // one-token lookahead on the per-token inputs
-    float4 k0n, k1n, q0n, q1n;
-    float vn[PASSES], gn = 1.f, bn = 0.f;
-    auto fetch = [&](int64_t t) {
+    // per-token inputs of tokens t .. t + LA - 1 in flight, token u in slot (u - t0) % LA
+    float4 k0n[LA], k1n[LA], q0n[LA], q1n[LA];
+    float vn[LA][PASSES], gn[LA], bn[LA];
+    auto fetch = [&](int j, int64_t t) {
         const int64_t th = t * H + h;
-        k0n = In<TIn>::load4(k + th * D + c0);
-        k1n = In<TIn>::load4(k + th * D + c1);
-        q0n = In<TIn>::load4(q + th * D + c0);
-        q1n = In<TIn>::load4(q + th * D + c1);
+        k0n[j] = In<TIn>::load4(k + th * D + c0);
+        k1n[j] = In<TIn>::load4(k + th * D + c1);
+        q0n[j] = In<TIn>::load4(q + th * D + c0);
+        q1n[j] = In<TIn>::load4(q + th * D + c1);
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) vn[p] = In<TIn>::load1(v + th * D + rowp[p]);
-        gn = g ? g[th] : 1.f;
-        bn = beta[th];
+        for (int p = 0; p < PASSES; ++p) vn[j][p] = In<TIn>::load1(v + th * D + rowp[p]);
+        gn[j] = g ? g[th] : 1.f;
+        bn[j] = beta[th];
     };
-    if (t0 < t1) fetch(t0);
-    for (int64_t t = t0; t < t1; ++t) {
-        const float4 k0 = k0n, k1 = k1n, q0 = q0n, q1 = q1n;
-        float vr[PASSES];
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) vr[p] = vn[p];
-        const float gt = gn, bt = bn;
-        if (t + 1 < t1) fetch(t + 1);
-        const float kq = group_sum<L::LPR>(dot4(k0, q0) + dot4(k1, q1));
-        float* orow = o + (t * H + h) * (int64_t)D;
+    for (int j = 0; j < LA; ++j)
+        if (t0 + j < t1) fetch(j, t0 + j);
+    for (int64_t tb = t0; tb < t1; tb += LA) {
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const float a = group_sum<L::LPR>(dot4(s0[p], k0) + dot4(s1[p], k1));
-            const float b = group_sum<L::LPR>(dot4(s0[p], q0) + dot4(s1[p], q1));
-            const float c = bt * (vr[p] - (erase ? a : 0.f));
-            s0[p] = axpby4(gt, s0[p], c, k0);
-            s1[p] = axpby4(gt, s1[p], c, k1);
-            if (okp[p] && lr == 0) orow[rowp[p]] = gt * b + c * kq;
+        for (int j = 0; j < LA; ++j) {
+            const int64_t t = tb + j;
+            if (t >= t1) break;
+            const float4 k0 = k0n[j], k1 = k1n[j], q0 = q0n[j], q1 = q1n[j];
+            float vr[PASSES];
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p) vr[p] = vn[j][p];
+            const float gt = gn[j], bt = bn[j];
+            if (t + LA < t1) fetch(j, t + LA);
+            const float kq = group_sum<L::LPR>(dot4(k0, q0) + dot4(k1, q1));
+            float *orow = o + (t * H + h) * (int64_t)D;
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p) {
+                const float a = group_sum<L::LPR>(dot4(s0[p], k0) + dot4(s1[p], k1));
+                const float b = group_sum<L::LPR>(dot4(s0[p], q0) + dot4(s1[p], q1));
+                const float c = bt * (vr[p] - (erase ? a : 0.f));
+                s0[p] = axpby4(gt, s0[p], c, k0);
+                s1[p] = axpby4(gt, s1[p], c, k1);
+                if (okp[p] && lr == 0) orow[rowp[p]] = gt * b + c * kq;
+            }
         }
     }
 #pragma unroll
@@ -207,7 +217,14 @@ static constexpr int decode_waves(int d) { return d >= 64 ? 4 : 1; }
 // plain copy kernel streams best with about four loads per lane and many
 // workgroups, too).
 static constexpr int decode_split(int d) { return d == 128 ? 4 : 1; }
-static constexpr int serial_tiles(int d) { return d >= 32 ? d / 32 : 1; }
+// Rows per workgroup of the serial prefill: at d = 128, 8 (16 workgroups per
+// (sequence, head)); measured at T = 4096, H = 48, fp32, one token of inputs
+// in flight: 32 rows 5.02 ms, 16 rows 2.92, 8 rows 2.69, 4 rows 3.08.  Smaller
+// heads keep 32 (or all) rows.  Tokens of inputs in flight (8 rows): 1 token
+// 2.69 ms, 2 tokens 2.00, 4 tokens 2.01, 8 tokens 1.88.
+static constexpr int serial_rows(int d) { return d == 128 ? 8 : d >= 32 ? 32 : d; }
+static constexpr int serial_tiles(int d) { return d / serial_rows(d); }
+constexpr int SERIAL_LOOKAHEAD = 8;
 
 bool decode_fits(int d, int64_t BH) { return launch_fits(BH * decode_split(d), 64 * decode_waves(d)); }
 bool prefill_serial_fits(int d, int64_t n_seq, int H) { return launch_fits(n_seq * H * serial_tiles(d), 64); }
@@ -253,11 +270,11 @@ template <typename TIn, int D>
 static hipError_t serial_d(const void *q, const void *k, const void *v, const float *g, const float *beta,
                            const int32_t *cu, int64_t n_seq, int64_t total, int H, const float *s_in, float *o,
                            float *s_out, int erase, hipStream_t stream) {
-    constexpr int ROWS = D >= 32 ? 32 : D;
+    constexpr int ROWS = serial_rows(D);
     static_assert(D / ROWS == serial_tiles(D), "row tiles per (sequence, head)");
     const int64_t blocks = n_seq * H * (D / ROWS);
     if (!launch_fits(blocks, 64)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_prefill_serial<TIn, D, ROWS>), dim3((unsigned)blocks), dim3(64), 0, stream,
+    hipLaunchKernelGGL((k_prefill_serial<TIn, D, ROWS, SERIAL_LOOKAHEAD>), dim3((unsigned)blocks), dim3(64), 0, stream,
                        (const TIn *)q, (const TIn *)k, (const TIn *)v, g, beta, cu, total, H, s_in, o, s_out, erase);
     return hipGetLastError();
 }
