@@ -85,6 +85,21 @@ def test_serial_varlen(oracle_lib, dtype, d):
     assert np.array_equal(s[1], inp.s_init[1])  # zero-length sequence keeps its state
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_serial_lookahead_edges(oracle_lib, dtype):
+    """The token-serial kernel keeps the inputs of the next 8 tokens in flight
+    (its loop unrolled by 8): sequences of 1 to 17 tokens, on both sides of
+    each multiple of 8, packed in one batch at d = 128 (8-row tiles)."""
+    say("serial lookahead edges", dtype)
+    inp = w.make_prefill([7, 8, 9, 1, 15, 16, 17, 2], H=2, d=128, dtype=dtype, seed=71, gate_shift=-2.0,
+                         init_std=0.3)
+    o, s = gpu_prefill(inp, chunk=gdn.CHUNK_SERIAL)
+    o_ref, s_ref = oracle_prefill(inp)
+    tol = tol_for(dtype)
+    assert rel_max_err(o, o_ref) <= tol
+    assert rel_max_err(s, s_ref) <= tol
+
+
 def test_serial_in_place_state(oracle_lib):
     inp = w.make_prefill([50, 20], H=2, d=64, dtype="fp32", seed=5, init_std=0.2)
     d = {k: v for k, v in zip(["q", "k", "v"], [w.to_torch(x, "fp32", DEV) for x in (inp.q, inp.k, inp.v)])}
