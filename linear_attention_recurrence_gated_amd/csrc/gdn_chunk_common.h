@@ -5,9 +5,9 @@
 // call; gdn_chain.hip holds the state chains and the scan's combine, compiled
 // with the instruction scheduler set for instruction-level parallelism (the
 // chains run one wave per SIMD through a serial chain of dependent products:
-// measured 112.8 against 117.5 us per call at T = 4096, H = 48, where the
-// preparation kernel, with four workgroups per CU, measured 57.0 against 42.2
-// us under that setting, so it keeps the default).
+// at T = 4096, H = 48 the chain measured 112.5 against 117.4 us, the call 149.8
+// against 155.0 us; the preparation kernel, four workgroups per CU, measured
+// 57.0 against 42.2 us under that setting, so it keeps the default).
 #pragma once
 
 #include <algorithm>
