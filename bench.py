@@ -161,7 +161,7 @@ def bench_prefill(torch, gdn, w, steps, warmup, rotate):
     """Times `steps` prefill steps cycling over `rotate` resident copies of the
     inputs and outputs (rotate > 1 keeps the 256 MB last-level cache from
     serving one step's inputs to the next)."""
-    inp = w.config2(T=T, H=H, d=D)
+    inp = w.prefill_t4096_h48(T=T, H=H, d=D)
     dev = "cuda:0"
     q0 = w.to_torch(inp.q, "bf16", dev)
     k0 = w.to_torch(inp.k, "bf16", dev)
@@ -210,7 +210,7 @@ def bench_decode(torch, gdn, w, steps, rotate):
     """One pass of `steps` decode steps; step t updates state copy t % rotate
     (rotate > 1 stands for successive layers, each with its own state, so the
     192 MiB state is not served from the last-level cache)."""
-    dec = w.config3(steps=steps, B=DEC_B, H=H, d=D)
+    dec = w.decode_b64_h48(steps=steps, B=DEC_B, H=H, d=D)
     dev = "cuda:0"
     q = w.to_torch(dec.q, "bf16", dev)
     k = w.to_torch(dec.k, "bf16", dev)
@@ -278,7 +278,7 @@ def bench_decode_slots(torch, gdn, w, steps, rotate):
     iteration over `rotate` layers, as a server would capture it); returns
     (eager, graph), each (block ms per step, sorted per-call ms)."""
     import numpy as np
-    dec = w.config3(steps=1, B=DEC_B, H=H, d=D)
+    dec = w.decode_b64_h48(steps=1, B=DEC_B, H=H, d=D)
     dev = "cuda:0"
     n_slots = 2 * DEC_B
     q = w.to_torch(dec.q[0], "bf16", dev)
@@ -411,13 +411,13 @@ def layer_entry(layer_ms, two_ms, kern):
                          "traffic": None if tl is None or tc is None else tl + tc}}
 
 
-def bench_config4(torch, gdn, w, runs):
+def bench_long_context(torch, gdn, w, runs):
     """Long-context prefill: 262,144 tokens (H = 48) as 16 segments of 16,384
     with the fp32 state carried from each call to the next, in place; inputs
     resident (all 16 segments).  Returns (sorted per-run ms, tokens)."""
     dev = "cuda:0"
     segs = []
-    for seg in w.config4_segments():
+    for seg in w.long_context_segments():
         segs.append((w.to_torch(seg.q, "bf16", dev), w.to_torch(seg.k, "bf16", dev), w.to_torch(seg.v, "bf16", dev),
                      torch.from_numpy(seg.g).to(dev), torch.from_numpy(seg.beta).to(dev)))
         del seg
@@ -460,10 +460,10 @@ def bench_config4(torch, gdn, w, runs):
     return sorted(times), N1, one_shot, ws_bytes
 
 
-def bench_config5(torch, gdn, w, steps, warmup):
+def bench_varlen(torch, gdn, w, steps, warmup):
     """Variable-length packed prefill: 8 sequences (130,093 tokens), H = 48,
     per-sequence initial states; back-to-back calls timed as a block."""
-    inp = w.config5()
+    inp = w.varlen_batch()
     dev = "cuda:0"
     q, k, v = (w.to_torch(x, inp.dtype, dev) for x in (inp.q, inp.k, inp.v))
     g, b = torch.from_numpy(inp.g).to(dev), torch.from_numpy(inp.beta).to(dev)
@@ -553,7 +553,7 @@ def cpu_baseline(w, seconds):
     from oracle import build as oracle_build
     if not os.path.exists(oracle.LIB_PATH):
         oracle_build.build()
-    inp = w.config2(T=T, H=H, d=D)
+    inp = w.prefill_t4096_h48(T=T, H=H, d=D)
     threads = oracle.default_threads()
     runs, t0 = 0, time.perf_counter()
     while True:
@@ -587,7 +587,7 @@ def pre_entry(pre_block_ms, pre_ms):
 
 
 def long_entry(run_ms, tokens, one_shot_ms=None, one_shot_ws=None):
-    """Config 4: 16 calls of 16,384 tokens, the state carried (read and written by each call)."""
+    """The long-context prefill: 16 calls of 16,384 tokens, the state carried (read and written by each call)."""
     nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * tokens * H + 16 * 2 * STATE_BYTES_PER_HEAD * H
     ms = mean(run_ms)
     gbs = nbytes / (ms / 1e3) / 1e9
@@ -600,7 +600,7 @@ def long_entry(run_ms, tokens, one_shot_ms=None, one_shot_ws=None):
 
 
 def varlen_entry(ms, tokens, n_seq):
-    """Config 5: one call over the packed batch, initial and final states per sequence."""
+    """The varlen prefill: one call over the 8-sequence packed batch, initial and final states per sequence."""
     nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * tokens * H + n_seq * 2 * STATE_BYTES_PER_HEAD * H
     gbs = nbytes / (ms / 1e3) / 1e9
     return {"workload": f"{n_seq} packed sequences, log-uniform lengths in [1024, 65536] ({tokens} tokens), H = 48, "
@@ -627,15 +627,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of parts to time alone (prefill, decode, decode_slots, preprocess, scan, config4, "
-                         "config5, fp32, plan, layer, copy), one JSON line each, for profiling runs; 'copy' is the "
+                    help="comma list of parts to time alone (prefill, decode, decode_slots, preprocess, scan, long_context, "
+                         "varlen, fp32, plan, layer, copy), one JSON line each, for profiling runs; 'copy' is the "
                          "byte-counter calibration copy")
     ap.add_argument("--warm", action="store_true",
                     help="also time one resident copy (inputs and state may then sit in the last-level cache)")
     ap.add_argument("--rotate", type=int, default=4,
                     help="resident copies of the inputs/states cycled through by successive steps")
     ap.add_argument("--copy-mib", type=float, default=1024.0, help="size of the calibration copy")
-    ap.add_argument("--config4-runs", type=int, default=3, help="full 16-segment runs of the long-context prefill")
+    ap.add_argument("--long-context-runs", type=int, default=3, help="full 16-segment runs of the long-context prefill")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the recurrence shards across heads and sequences with no "
@@ -653,7 +653,7 @@ def main():
     if args.only:
         parts = args.only.split(",")
         bad = [p for p in parts if p not in ("prefill", "decode", "decode_slots", "preprocess", "scan", "copy",
-                                             "config4", "config5", "fp32", "plan", "layer")]
+                                             "long_context", "varlen", "fp32", "plan", "layer")]
         if bad:
             ap.error(f"--only: unknown part(s) {bad}")
         for part in parts:
@@ -676,13 +676,13 @@ def main():
                 pre_block, pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
                 print(json.dumps({"only": "preprocess", "ms_per_call": pre_block,
                                   "event_bracketed_mean_ms": mean(pre_ms)}), flush=True)
-            elif part == "config4":
-                c4_ms, c4_tok, c4_one, c4_ws = bench_config4(torch, gdn, w, args.config4_runs)
-                print(json.dumps({"only": "config4", "run_ms": c4_ms, "tokens": c4_tok, "one_call_ms": c4_one,
-                                  "one_call_workspace_bytes": c4_ws}), flush=True)
-            elif part == "config5":
-                c5_ms, c5_tok, _ = bench_config5(torch, gdn, w, args.steps, args.warmup)
-                print(json.dumps({"only": "config5", "ms_per_call": c5_ms, "tokens": c5_tok}), flush=True)
+            elif part == "long_context":
+                lc_ms, lc_tok, lc_one, lc_ws = bench_long_context(torch, gdn, w, args.long_context_runs)
+                print(json.dumps({"only": "long_context", "run_ms": lc_ms, "tokens": lc_tok, "one_call_ms": lc_one,
+                                  "one_call_workspace_bytes": lc_ws}), flush=True)
+            elif part == "varlen":
+                vl_ms, vl_tok, _ = bench_varlen(torch, gdn, w, args.steps, args.warmup)
+                print(json.dumps({"only": "varlen", "ms_per_call": vl_ms, "tokens": vl_tok}), flush=True)
             elif part == "fp32":
                 print(json.dumps({"only": "fp32", "ms_per_call": bench_fp32(torch, gdn, w, max(3, args.steps // 10))}),
                       flush=True)
@@ -699,8 +699,8 @@ def main():
     pre_block, pre_ms = bench_preprocess(torch, gdn, w, args.steps, args.warmup, args.rotate)
     (ds_block, ds_ms), (dg_block, dg_ms) = bench_decode_slots(torch, gdn, w, args.decode_steps, args.rotate)
     scan = bench_scan(torch, gdn, w, min(args.steps, 20), args.warmup)
-    c4_ms, c4_tok, c4_one, c4_ws = bench_config4(torch, gdn, w, args.config4_runs)
-    c5_ms, c5_tok, c5_nseq = bench_config5(torch, gdn, w, min(args.steps, 20), args.warmup)
+    lc_ms, lc_tok, lc_one, lc_ws = bench_long_context(torch, gdn, w, args.long_context_runs)
+    vl_ms, vl_tok, vl_nseq = bench_varlen(torch, gdn, w, min(args.steps, 20), args.warmup)
     fp32_ms = bench_fp32(torch, gdn, w, 5)
     layer_ms, layer_two_ms, layer_kern = bench_layer(torch, gdn, w, args.steps, args.warmup, args.rotate)
 
@@ -775,11 +775,11 @@ def main():
                          "value": dec_bytes / (ds_block / 1e3) / 1e9, "unit": "GB/s",
                          "frac_hbm_peak": dec_bytes / (ds_block / 1e3) / 1e9 / HBM_PEAK_GBS,
                          "graph_replay_ms_per_step": dg_block, "graph_replay_p50_ms": pct(dg_ms, 50),
-                         "workload": "config-3 step, 64 rows on a permutation of 64 of 128 pool slots; eager "
+                         "workload": "decode step at B = 64, H = 48, d = 128, 64 rows on a permutation of 64 of 128 pool slots; eager "
                                      "launches, and replays of one captured HIP graph holding one step per pool "
                                      "(per-step time = replay time / pools); each timed as a block"},
-        "config4": long_entry(c4_ms, c4_tok, c4_one, c4_ws),
-        "config5": varlen_entry(c5_ms, c5_tok, c5_nseq),
+        "long_context": long_entry(lc_ms, lc_tok, lc_one, lc_ws),
+        "varlen": varlen_entry(vl_ms, vl_tok, vl_nseq),
         "fp32_prefill": fp32_entry(fp32_ms),
         "layer": layer_entry(layer_ms, layer_two_ms, layer_kern),
         "rotate": args.rotate,

@@ -203,25 +203,26 @@ def make_decode(steps, B, H, d, dtype="bf16", seed=SEED_BASE + 3, gate_shift=2.0
 
 
 # ---------------------------------------------------------------------------
-# The five workloads.  Indices 1..5 follow the order in which the workloads are
-# listed in the project's configuration.
+# The five workloads, numbered 1..5 for their seeds (SeedSequence(1000 + n)):
+# a tiny fp32 prefill, the one-layer prefill at T = 4096, batched decode, the
+# long context in segments, and a packed varlen batch.
 
-def config1():
+def prefill_t64_d16_fp32():
     """Single head, fp32: B=1, H=1, T=64, d=16, g = exp(-softplus(x)), S_0 = 0."""
     return make_prefill([64], H=1, d=16, dtype="fp32", seed=SEED_BASE + 1, gate_shift=0.0)
 
 
-def config2(T=4096, H=48, d=128, seed=SEED_BASE + 2, gate_shift=2.0):
+def prefill_t4096_h48(T=4096, H=48, d=128, seed=SEED_BASE + 2, gate_shift=2.0):
     """One-layer prefill: B=1, H=48, T=4096, d=128, bf16, S_0 = 0, chunk 64."""
     return make_prefill([T], H=H, d=d, dtype="bf16", seed=seed, gate_shift=gate_shift)
 
 
-def config3(steps=256, B=64, H=48, d=128):
+def decode_b64_h48(steps=256, B=64, H=48, d=128):
     """Batched decode: B=64, H=48, d=128, 256 single-token steps, S_0 ~ N(0, 0.02^2)."""
     return make_decode(steps, B, H, d, dtype="bf16", seed=SEED_BASE + 3)
 
 
-def config4_segments(n_seg=16, seg_len=16384, H=48, d=128):
+def long_context_segments(n_seg=16, seg_len=16384, H=48, d=128):
     """Long context: 262,144 tokens as 16 segments of 16,384 with the state
     carried; segment i is drawn from child stream i of SeedSequence(1004)."""
     children = np.random.SeedSequence(SEED_BASE + 4).spawn(n_seg)
@@ -231,17 +232,17 @@ def config4_segments(n_seg=16, seg_len=16384, H=48, d=128):
                             meta=dict(segment=i, seg_len=seg_len, H=H, d=d))
 
 
-def config5_lengths(n=8, lo=1024, hi=65536):
+def varlen_lengths(n=8, lo=1024, hi=65536):
     ss = np.random.SeedSequence(SEED_BASE + 5)
     len_ss, _ = ss.spawn(2)
     return [int(x) for x in log_uniform_lengths(np.random.default_rng(len_ss), n, lo, hi)]
 
 
-def config5(H=48, d=128):
+def varlen_batch(H=48, d=128):
     """Variable-length packed prefill: 8 sequences, log-uniform lengths in
     [1024, 65536], per-sequence initial states ~ N(0, 0.02^2), reset between
     sequences, per-sequence final states."""
-    lengths = config5_lengths()
+    lengths = varlen_lengths()
     _, data_ss = np.random.SeedSequence(SEED_BASE + 5).spawn(2)
     tok_ss, state_ss = data_ss.spawn(2)
     N = sum(lengths)

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 
 def test_decode_step_time_is_flat_over_256_steps():
-    dec = w.config3()
+    dec = w.decode_b64_h48()
     steps = dec.q.shape[0]
     q, k, v = (w.to_torch(x, "bf16", DEV) for x in (dec.q, dec.k, dec.v))
     g, beta = torch.from_numpy(dec.g).to(DEV), torch.from_numpy(dec.beta).to(DEV)

@@ -43,7 +43,7 @@ def test_decode_full_size_sampled(oracle_lib):
     """B=64, H=48, d=128, 256 steps in place (the decode workload), checked on
     sampled sequences: the oracle replays those sequences' 256 tokens."""
     say("decode full size B=64 H=48 d=128 steps=256")
-    dec = w.config3()
+    dec = w.decode_b64_h48()
     o, s = run_decode_gpu(dec)
     pick = [0, 17, 63]
     o_ref, s_ref = oracle_lib.run_decode(dec.q[:, pick], dec.k[:, pick], dec.v[:, pick], dec.g[:, pick],
@@ -62,9 +62,9 @@ def test_decode_is_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def test_config1_serial_fp32(oracle_lib):
-    say("config1 fp32 d=16 T=64")
-    inp = w.config1()
+def test_tiny_fp32_d16_serial(oracle_lib):
+    say("fp32 d=16 T=64")
+    inp = w.prefill_t64_d16_fp32()
     assert gdn.prefill_algorithm(gdn.GDN_FP32, 16, 16) == gdn.CHUNK_SERIAL
     o, s = gpu_prefill(inp)
     o_ref, s_ref = oracle_prefill(inp)

@@ -27,8 +27,8 @@ def test_same_seed_same_bytes():
     assert c.q.tobytes() != a.q.tobytes()
 
 
-def test_config1_shapes_and_ranges():
-    c = w.config1()
+def test_tiny_fp32_shapes_and_ranges():
+    c = w.prefill_t64_d16_fp32()
     assert c.q.shape == (64, 1, 16) and c.v.shape == (64, 1, 16) and c.g.shape == (64, 1)
     assert c.dtype == "fp32" and c.cu_seqlens is None and c.s_init is None
     assert np.allclose(np.linalg.norm(c.k.astype(np.float64), axis=-1), 1.0, atol=1e-6)
@@ -36,7 +36,7 @@ def test_config1_shapes_and_ranges():
 
 
 def test_prefill_bf16_values_are_exact_and_normalised():
-    c = w.config2(T=256, H=4)
+    c = w.prefill_t4096_h48(T=256, H=4)
     for x in (c.q, c.k, c.v):
         w.bf16_bits(x)  # raises if any value is not bf16-exact
     n = np.linalg.norm(c.k.astype(np.float64), axis=-1)
@@ -45,10 +45,10 @@ def test_prefill_bf16_values_are_exact_and_normalised():
     assert -3.0 < lg.mean() < -1.5  # g = exp(-softplus(x + 2)): strong decay
 
 
-def test_config5_lengths_in_range_and_fixed():
-    lens = w.config5_lengths()
+def test_varlen_lengths_in_range_and_fixed():
+    lens = w.varlen_lengths()
     assert len(lens) == 8 and all(1024 <= x <= 65536 for x in lens)
-    assert lens == w.config5_lengths()
+    assert lens == w.varlen_lengths()
 
 
 def test_decode_shapes():
