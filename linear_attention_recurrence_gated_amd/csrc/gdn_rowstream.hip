@@ -153,6 +153,14 @@ __global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q
     }
 
     // per-token inputs, token tb + j in slot j
+    // g and beta go through vector loads too (a lane offset that the compiler
+    // cannot see is zero): scalar loads may return out of order, so a wait for
+    // one of them waits for all, the newest included.  Without g, beta's value
+    // stands in (a load that is never used, so that the loop has no branch).
+    const bool has_g = g != nullptr;
+    const float *gsrc = has_g ? g : beta;
+    int zero = 0;
+    asm volatile("" : "+v"(zero));
     float4 k0n[LA], k1n[LA], q0n[LA], q1n[LA];
     float vn[LA][PASSES], gn[LA], bn[LA];
     auto fetch = [&](int j, int64_t t) {  // t is wave-uniform
@@ -164,11 +172,11 @@ __global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q
         q1n[j] = In<TIn>::load4(qt + c1);
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) vn[j][p] = In<TIn>::load1(vt + rowp[p]);
-        gn[j] = g ? g[th] : 1.f;
-        bn[j] = beta[th];
+        gn[j] = gsrc[th + zero];
+        bn[j] = beta[th + zero];
     };
     auto token = [&](int j, int64_t t) {
-        const float gt = gn[j], bt = bn[j];
+        const float gt = has_g ? gn[j] : 1.f, bt = bn[j];
         const float kq = group_sum<L::LPR>(dot4(k0n[j], q0n[j]) + dot4(k1n[j], q1n[j]));
         float *orow = o + (t * H + h) * (int64_t)D;
 #pragma unroll
@@ -178,15 +186,21 @@ __global__ __launch_bounds__(64) void k_prefill_serial(const TIn *__restrict__ q
             const float c = bt * (vn[j][p] - (erase ? a : 0.f));
             s0[p] = axpby4(gt, s0[p], c, k0n[j]);
             s1[p] = axpby4(gt, s1[p], c, k1n[j]);
-            if (okp[p] && lr == 0) orow[rowp[p]] = gt * b + c * kq;
+            // every lane of a row holds the row's output: with whole passes all
+            // of them store it (one store, no branch), else only the valid rows
+            if constexpr (ROWS % L::RPP == 0) orow[rowp[p]] = gt * b + c * kq;
+            else if (okp[p]) orow[rowp[p]] = gt * b + c * kq;
         }
     };
     if (t1 > t0) {
 #pragma unroll
         for (int j = 0; j < LA; ++j) fetch(j, min(t0 + j, t1 - 1));
     }
-    // Full blocks of LA tokens, with no exit inside a block, then the rest
-    // (an exit test after every token cost 8% at T = 4096, H = 48, fp32).
+    // Full blocks of LA tokens, with no exit inside a block and no branch at
+    // all, then the rest: a branch inside the loop (an exit test per token, a
+    // test of g, a store by one lane of each row) made the compiler move the
+    // slots' registers at the loop's back edge, waiting there for the newest
+    // loads once per block.
     int64_t tb = t0;
     for (; tb + LA <= t1; tb += LA) {
 #pragma unroll
@@ -233,7 +247,7 @@ static constexpr int decode_split(int d) { return d == 128 ? 4 : 1; }
 // 2.69 ms, 2 tokens 2.00, 4 tokens 2.01, 8 tokens 1.88; with each slot
 // refilled after its token and the full blocks free of exit tests, 1.58 ms
 // (same bits; 4 rows with 8 or 12 tokens in flight 3.20 and 1.83 ms before
-// that change).
+// that change); with no branch in the loop (below), see the kernel's notes.
 static constexpr int serial_rows(int d) { return d == 128 ? 8 : d >= 32 ? 32 : d; }
 static constexpr int serial_tiles(int d) { return d / serial_rows(d); }
 constexpr int SERIAL_LOOKAHEAD = 8;
